@@ -1,0 +1,31 @@
+"""Shared pytest set-up: the ``gpu`` marker and repository imports.
+
+Tests marked ``gpu`` need an MI355X and the built HIP library. Where no GPU is
+visible they are skipped; where a GPU is visible they run, and a missing or
+unloadable library fails them loudly (there is no CPU fallback).
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available() and torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if _gpu_present():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
