@@ -1,0 +1,195 @@
+/*
+ * pa.h — C ABI of the paged KV-cache attention library (gfx950 / MI355X).
+ *
+ * The operation: attention of each query token over a key/value cache that is
+ * stored in fixed-size physical blocks and reached through a per-sequence
+ * block table, plus the write of new tokens' K/V into the slots a block
+ * manager chose. Sources, by page title and section:
+ *   [P1] "vLLM推理引擎深度解析：从PagedAttention原理到高吞吐量部署的工程实践"
+ *        §三 (PagedAttentionManager: block pool, block tables, append_token,
+ *        share_prefix) and §五 (PagedAttention.forward: per sequence, look up
+ *        the block table, read K and V from the physical blocks, scores
+ *        q·k / sqrt(head_dim), softmax, weighted sum of V).
+ *   [P2] "vLLM 原理与源码阅读", PagedAttention 显存管理 → Block 管理器
+ *        (one block table per request, 16 tokens per block by default,
+ *        copy-on-write for shared prefix blocks).
+ *   [P3] "vLLM推理引擎深度实战", §1.2 PagedAttention原理 (BLOCK_SIZE = 16,
+ *        a block holds K and V of its tokens for all heads) and §5.3
+ *        推理优化配置 (the chunked-prefill switch).
+ *
+ * Common conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     `stream`, which is a hipStream_t passed as void* (NULL = null stream).
+ *     The library allocates nothing, frees nothing, keeps no pointer after it
+ *     returns and has no mutable global state; calls are thread-safe.
+ *   - Every call only enqueues work on `stream` and returns; stream order is
+ *     what makes a cache write visible to a later attention call.
+ *   - `dtype` is a pa_dtype_t. Element types: F32 = float, F16 = IEEE half,
+ *     BF16 = bfloat16. All arithmetic accumulates in fp32; outputs are rounded
+ *     to `dtype` with round-to-nearest-even.
+ *   - K/V pool layout: physical block i of the K pool starts at element
+ *     `k_cache + i * block_stride` and holds `[block_size][num_kv_heads]
+ *     [head_dim]` contiguous elements, token-major as the per-block K and V
+ *     planes of [P1] §五. The V pool is laid out the same way at `v_cache`.
+ *     P1's interleaved per-block (2, block_size, heads, head_dim) tensor is
+ *     the case v_cache = k_cache + block_size*num_kv_heads*head_dim and
+ *     block_stride = 2*block_size*num_kv_heads*head_dim.
+ *   - Block tables: int32 `[num_seqs][block_table_stride]`; entry i of row b is
+ *     the physical block that holds logical block i (tokens 16i .. 16i+15) of
+ *     sequence b. Only the first ceil(L_b / block_size) entries are read.
+ *   - Supported shapes: block_size == 16; head_dim in {64, 128};
+ *     num_q_heads % num_kv_heads == 0 with group G = num_q_heads/num_kv_heads
+ *     in {1, 2, 4, 8}. Pointers must be 16-byte aligned and strides must be
+ *     multiples of 16 bytes.
+ *
+ * Errors: every entry point returns a pa_status_t and never aborts. The host
+ * checks O(1) arguments only (NULL pointers, enums, supported shapes,
+ * alignment, workspace size). The CONTENTS of device index arrays are
+ * preconditions: non-negative slots unique and < num_blocks*block_size;
+ * tables covering ceil(L/16) entries < num_blocks; 0 <= L. The kernels never
+ * read or write outside the pools when these are violated (out-of-range slots
+ * are skipped, out-of-range table entries are read as block 0 and masked),
+ * but the affected results are then undefined. `num_seqs == 0` (or
+ * `num_tokens == 0`) returns PA_OK without launching.
+ */
+#ifndef PAGED_KV_CACHE_463_AMD_PA_H
+#define PAGED_KV_CACHE_463_AMD_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the C ABI are the only ones the shared library exports. */
+#define PA_API __attribute__((visibility("default")))
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                          */
+  PA_ERR_DTYPE = 2,        /* dtype is not a pa_dtype_t, or not supported here    */
+  PA_ERR_SHAPE = 3,        /* a size or stride is negative or inconsistent        */
+  PA_ERR_UNSUPPORTED = 4,  /* block_size, head_dim or group size not supported    */
+  PA_ERR_WORKSPACE = 5,    /* split-KV workspace missing or too small             */
+  PA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch         */
+  PA_ERR_ALIGNMENT = 7     /* a pointer or stride is not 16-byte aligned          */
+} pa_status_t;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+PA_API const char* pa_status_string(int32_t status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+PA_API int32_t pa_version(void);
+
+/*
+ * pa_reshape_and_cache — write new tokens' K and V into their cache slots.
+ * [P1] §三 append_token fixes where a new token goes (the last block of the
+ * sequence while it has room, else a fresh block); [P1] §五 leaves the write
+ * itself to the block manager. Slot s names physical block s / block_size,
+ * row s % block_size.
+ *
+ *   key, value       [num_tokens][num_kv_heads][head_dim], row t at element
+ *                    t * kv_token_stride (heads and dims contiguous in a row)
+ *   kv_token_stride  elements between consecutive token rows (>= H_kv*D)
+ *   k_cache, v_cache pools (layout above), written in place
+ *   block_stride     elements between consecutive physical blocks (>= 16*H_kv*D)
+ *   num_blocks       physical blocks in each pool
+ *   slot_mapping     int32 [num_tokens]; negative entries are skipped
+ *   dtype            any pa_dtype_t; the copy is bit-exact
+ * slot_mapping may be NULL only when num_tokens == 0. Non-negative slots must
+ * be unique (duplicates race; the result is then undefined).
+ */
+PA_API int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
+                             void* k_cache, void* v_cache, int64_t block_stride,
+                             int64_t num_blocks, const int32_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t dtype, void* stream);
+
+/*
+ * pa_decode — one query token per sequence attends over its cached tokens
+ * ([P1] §五 PagedAttention.forward), single pass over the KV cache.
+ *
+ *   out              [num_seqs][num_q_heads][head_dim], dtype; must not alias inputs
+ *   query            [num_seqs][num_q_heads][head_dim], dtype
+ *   k_cache, v_cache pools (layout above), dtype
+ *   block_tables     int32 [num_seqs][block_table_stride]
+ *   context_lens     int32 [num_seqs]: L_b, tokens in cache INCLUDING this
+ *                    step's new token (written by pa_reshape_and_cache first);
+ *                    every cached position precedes the query, so no mask.
+ *                    L_b == 0 yields an all-zero output row.
+ *   scale            score scale (1/sqrt(head_dim) in [P1] §五)
+ * Query head h reads K/V head h / G (contiguous groups; with G == 1 this is
+ * the multi-head case of the pages).
+ */
+PA_API int32_t pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                  int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                  int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, float scale, int32_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode_splitkv needs: per (sequence, query
+ * head, partition) one fp32 partial output row of head_dim plus its running
+ * max and normaliser. Returns 0 for non-positive sizes.
+ */
+PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode_splitkv — pa_decode for long contexts: the cached tokens of each
+ * sequence are cut into partitions of `partition_size` logical tokens, each
+ * partition computes (max score, sum of exponentials, unnormalised output),
+ * and a second kernel merges them by log-sum-exp. The merged result is the
+ * same softmax as pa_decode (the decomposition is exact in exact arithmetic).
+ *
+ * Arguments as pa_decode, plus
+ *   max_context_len  upper bound of context_lens (host-known); sequences
+ *                    longer than this are a precondition violation
+ *   partition_size   tokens per partition, a positive multiple of 16
+ *   workspace        device buffer of at least
+ *                    pa_decode_splitkv_workspace_bytes(...) bytes, 16-byte
+ *                    aligned; contents on entry are ignored
+ */
+PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, const void* v_cache,
+                          int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                          int32_t block_table_stride, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                          int32_t max_context_len, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_chunked — a chunk of new query tokens per sequence attends over
+ * the sequence's cache (prior tokens plus the chunk itself, already written
+ * by pa_reshape_and_cache), on bf16/f16 matrix cores. The pages only name the
+ * chunked-prefill switch ([P3] §5.3); the reading implemented: sequence b owns
+ * query rows cu_q_lens[b] .. cu_q_lens[b+1]-1, and query i of the chunk sits
+ * at absolute position seq_lens[b] - q_len_b + i; with `causal` it sees keys
+ * 0 .. that position (itself included), otherwise all seq_lens[b] keys.
+ *
+ *   out              [num_q_tokens][num_q_heads][head_dim], dtype
+ *   query            [num_q_tokens][num_q_heads][head_dim], dtype
+ *   cu_q_lens        int32 [num_seqs + 1], cumulative chunk lengths, cu[0] = 0
+ *   max_q_len        upper bound of the chunk lengths (host-known)
+ *   num_q_tokens     cu_q_lens[num_seqs]
+ *   seq_lens         int32 [num_seqs], keys in cache INCLUDING the chunk
+ *   causal           0 or 1
+ *   dtype            PA_DTYPE_BF16 or PA_DTYPE_F16
+ * Preconditions beyond the common ones: 0 <= q_len_b <= min(max_q_len, seq_lens[b]).
+ */
+PA_API int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_lens,
+                           int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                           const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                           const int32_t* block_tables, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t causal, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_CACHE_463_AMD_PA_H */

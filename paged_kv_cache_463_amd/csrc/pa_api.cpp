@@ -1,0 +1,235 @@
+// C ABI of the paged-attention library: argument validation and dispatch.
+// Declarations, layouts and error behaviour are documented in include/pa.h.
+// Validation touches no HIP API, so every error path returns before any
+// device work is enqueued.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_DTYPE_F32: return 4;
+    case PA_DTYPE_F16: return 2;
+    case PA_DTYPE_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Checks shared by the attention entry points.
+int32_t check_attention_common(const void* out, const void* query, const void* k_cache,
+                               const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t dtype) {
+  if (elem_bytes(dtype) == 0) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
+      block_table_stride < 0)
+    return PA_ERR_SHAPE;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!group_supported(num_q_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (block_stride < (int64_t)block_size * num_kv_heads * head_dim) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !lens) return PA_ERR_NULL_PTR;
+  if (num_blocks == 0 || block_table_stride == 0) return PA_ERR_SHAPE;
+  const int e = elem_bytes(dtype);
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (block_stride * e) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  return PA_OK;
+}
+
+pa::DecodeParams make_decode_params(void* out, const void* query, const void* k_cache,
+                                    const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    float scale, int32_t dtype) {
+  pa::DecodeParams p{};
+  p.out = out;
+  p.query = query;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride * elem_bytes(dtype);
+  p.num_blocks = num_blocks;
+  p.block_tables = block_tables;
+  p.block_table_stride = block_table_stride;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.dtype = dtype;
+  p.scale = scale;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_PTR: return "PA_ERR_NULL_PTR: a required pointer is NULL";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown or unsupported dtype";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent size or stride";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: block_size, head_dim or group not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-KV workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch error";
+    case PA_ERR_ALIGNMENT: return "PA_ERR_ALIGNMENT: pointer or stride not 16-byte aligned";
+    default: return "unknown pa_status_t";
+  }
+}
+
+int32_t pa_version(void) { return kVersion; }
+
+int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
+                             void* k_cache, void* v_cache, int64_t block_stride,
+                             int64_t num_blocks, const int32_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t dtype, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (kv_token_stride < row || block_stride < block_size * row) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_PTR;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (kv_token_stride * e) % 16 != 0 || (block_stride * e) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::ScatterParams p{};
+  p.key = key;
+  p.value = value;
+  p.token_stride_bytes = kv_token_stride * e;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride * e;
+  p.num_slots = num_blocks * block_size;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.row_bytes = (int32_t)(row * e);
+  return hip_status(pa::launch_reshape_and_cache(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                  int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                  int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, float scale, int32_t dtype, void* stream) {
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      partition_size <= 0)
+    return 0;
+  const int64_t parts = ceil_div(max_context_len, partition_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+  // fp32 partial outputs, then (max, normaliser) pairs; both 16-byte aligned
+  const int64_t acc_bytes = ceil_div(rows * head_dim * 4, 256) * 256;
+  return (size_t)(acc_bytes + rows * 2 * 4);
+}
+
+int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, const void* v_cache,
+                          int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                          int32_t block_table_stride, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                          int32_t max_context_len, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  // all-empty batches still get their zero rows written by the merge kernel
+  const int32_t mcl = max_context_len > 0 ? max_context_len : 1;
+  const size_t need = pa_decode_splitkv_workspace_bytes(num_seqs, num_q_heads, head_dim, mcl,
+                                                        partition_size);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  p.partition_blocks = partition_size / 16;
+  p.max_parts = (int32_t)ceil_div(mcl, partition_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * p.max_parts;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     ceil_div(rows * head_dim * 4, 256) * 256);
+  return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_lens,
+                           int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                           const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                           const int32_t* block_tables, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t causal, int32_t dtype, void* stream) {
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, seq_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16) return PA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
+  if (max_q_len < 0 || num_q_tokens < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (!cu_q_lens) return PA_ERR_NULL_PTR;
+  pa::PrefillParams p{};
+  p.out = out;
+  p.query = query;
+  p.cu_q_lens = cu_q_lens;
+  p.max_q_len = max_q_len;
+  p.num_q_tokens = num_q_tokens;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride * elem_bytes(dtype);
+  p.num_blocks = num_blocks;
+  p.block_tables = block_tables;
+  p.block_table_stride = block_table_stride;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.dtype = dtype;
+  p.causal = causal;
+  p.scale = scale;
+  hipError_t e = pa::launch_prefill(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+}  // extern "C"

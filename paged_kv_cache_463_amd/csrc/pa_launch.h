@@ -1,0 +1,74 @@
+// Internal launcher interface between the C ABI (pa_api.cpp) and the kernel
+// translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct ScatterParams {
+  const void* key;
+  const void* value;
+  int64_t token_stride_bytes;
+  void* k_cache;
+  void* v_cache;
+  int64_t block_stride_bytes;
+  int64_t num_slots;            // num_blocks * block_size
+  const int32_t* slot_mapping;
+  int64_t num_tokens;
+  int32_t row_bytes;            // num_kv_heads * head_dim * element bytes
+};
+
+struct DecodeParams {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t block_stride_bytes;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t block_table_stride;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  float scale;
+  // split-KV only
+  int32_t partition_blocks;     // partition_size / 16
+  int32_t max_parts;            // ceil(max_context_len / partition_size)
+  float* ws_acc;                // [num_seqs][num_q_heads][max_parts][head_dim]
+  float* ws_ml;                 // [num_seqs][num_q_heads][max_parts][2]  (max, normaliser)
+};
+
+struct PrefillParams {
+  void* out;
+  const void* query;
+  const int32_t* cu_q_lens;
+  int32_t max_q_len;
+  int64_t num_q_tokens;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t block_stride_bytes;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t block_table_stride;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t causal;
+  float scale;
+};
+
+hipError_t launch_reshape_and_cache(const ScatterParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,72 @@
+"""GPU parity of pa_decode_splitkv (partition pass + log-sum-exp merge) through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_463_amd as P
+import workloads as W
+from gpu_cases import DeviceDecode, assert_close, assert_scatter_exact, oracle_decode, out_f64, say, i32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,G,D", [("bf16", 8, 128), ("f16", 1, 128), ("f32", 4, 64), ("bf16", 2, 64)])
+@pytest.mark.parametrize("part", [16, 64, 512])
+def test_splitkv_shapes(dtype, G, D, part):
+    hkv = 2 if G < 8 else 1
+    case = W.make_decode("split", dtype, [1, 16, 17, 100, 511, 512, 513, 1500], G * hkv, hkv, D,
+                         seed=200 + part + G)
+    say(f"case: splitkv {dtype} G={G} D={D} part={part}")
+    d = DeviceDecode(case)
+    d.scatter()
+    out = d.decode(split=part)
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    assert_close(out_f64(out), oracle_decode(case, kp, vp), dtype, f"splitkv part={part}")
+
+
+def test_single_partition_matches_single_pass_bitwise():
+    case = W.make_decode("onepart", "bf16", [3, 90, 400, 1000], 32, 8, 128, seed=31)
+    d = DeviceDecode(case)
+    d.scatter()
+    a = d.decode().clone()
+    b = d.decode(split=1024, out=torch.empty_like(a))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_length_and_caller_workspace():
+    case = W.make_decode("ws", "f16", [0, 700, 1], 16, 8, 128, seed=32)
+    d = DeviceDecode(case)
+    d.scatter()
+    need = P.splitkv_workspace_bytes(3, 16, 128, 700, 512)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")     # NaN-filled scratch
+    out = d.decode(split=512, workspace=ws)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    assert not got[0].any()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    assert_close(got[1:], oracle_decode(case, kp, vp, [1, 2]), "f16", "splitkv zero-length batch")
+
+
+def test_workspace_too_small_is_rejected():
+    case = W.make_decode("ws2", "bf16", [100, 200], 8, 8, 128, seed=33)
+    d = DeviceDecode(case)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(P.PagedAttentionError) as e:
+        d.decode(split=512, workspace=small)
+    assert e.value.status == 5
+
+
+def test_long_context_bf16_full_size_sampled():
+    case = W.long_context_bf16()
+    order = np.argsort(case.context_lens)
+    seqs = sorted({int(order[0]), int(order[-1]), 3})
+    say(f"case: long context split-KV, sampled sequences {seqs}, lens {case.context_lens.tolist()}")
+    d = DeviceDecode(case)
+    d.scatter()
+    out = d.decode(split=512)
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    del d
+    assert_close(out_f64(out)[seqs], oracle_decode(case, kp, vp, seqs), "bf16", "long-context split-KV")
