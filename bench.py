@@ -1,0 +1,294 @@
+"""Throughput of the paged-attention hot path on one MI355X.
+
+One step = one attention layer of one decode step (or one prefill chunk) over
+the whole batch: ``pa_reshape_and_cache`` of the new tokens, then the attention
+call, both on torch's current stream. The KV pool is replicated over
+``--layers`` independent copies and steps rotate through them, the way a model
+walks its layers, so repeated steps are not served from the 256 MB
+last-level cache. Inputs are seeded synthetic tensors resident in HBM before
+the timed region starts.
+
+Prints ONE JSON line: value = sequence-steps per second (decode) or query
+tokens per second (prefill) for the whole job, plus the roofline of the
+dominant kernel (algorithmic bytes or flops per launch divided by its average
+duration, measured with HIP events on the launch stream inside the timed
+region) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV GB/s, % of MI355X HBM peak, seq-steps/s"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6    # dense, 256 CUs at 2.4 GHz
+TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+WORKLOADS = {
+    # name -> (generator key in workloads.NAMED, attention call)
+    "llama2_7b_fp16_decode_b64": ("llama2_7b_fp16", "decode"),
+    "llama3_8b_gqa_bf16_decode_b256": ("llama3_8b_gqa_bf16", "decode"),
+    "long_ctx_bf16_splitkv_b8": ("long_context_bf16", "splitkv"),
+    "tiny_fp32_decode_b4": ("tiny", "decode"),
+    "chunked_prefill_bf16_16x2048p512": ("chunked_prefill_bf16", "prefill"),
+}
+DEFAULT_WORKLOAD = "llama2_7b_fp16_decode_b64"
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (what the operation must touch, independent of the kernel)
+# ----------------------------------------------------------------------------
+def decode_bytes(case, unique: bool) -> int:
+    """KV rows of every cached token (shared prefix blocks once if ``unique``),
+    plus query, output, the table entries read and the lengths."""
+    import workloads as W
+    e = W.ELEM_BYTES[case.dtype]
+    row = 2 * case.num_kv_heads * case.head_dim * e          # K and V of one token, all kv heads
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    if unique and case.shared_blocks:
+        tokens -= (len(case.sharers) - 1) * len(case.shared_blocks) * W.BLOCK_SIZE
+    qo = 2 * case.num_seqs * case.num_q_heads * case.head_dim * e
+    tables = 4 * sum(W.ceil_div(int(L), W.BLOCK_SIZE) for L in case.context_lens) + 4 * case.num_seqs
+    return tokens * row + qo + tables
+
+
+def kv_bytes(case, unique: bool) -> int:
+    import workloads as W
+    e = W.ELEM_BYTES[case.dtype]
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    if unique and getattr(case, "shared_blocks", None):
+        tokens -= (len(case.sharers) - 1) * len(case.shared_blocks) * W.BLOCK_SIZE
+    return tokens * 2 * case.num_kv_heads * case.head_dim * e
+
+
+def scatter_bytes(case) -> int:
+    import workloads as W
+    e = W.ELEM_BYTES[case.dtype]
+    n = len(case.slot_mapping)
+    return 2 * 2 * n * case.num_kv_heads * case.head_dim * e + 4 * n     # read + write, K and V
+
+
+def prefill_flops(case) -> int:
+    """4*D per (query head, visible key) pair: QK^T and PV, causal."""
+    pairs = 0
+    for b in range(case.num_seqs):
+        ql, L = int(case.q_lens[b]), int(case.seq_lens[b])
+        pos = L - ql + np.arange(ql)
+        pairs += int((pos + 1).sum())
+    return 4 * case.head_dim * case.num_q_heads * pairs
+
+
+# ----------------------------------------------------------------------------
+# device state and one step
+# ----------------------------------------------------------------------------
+class Runner:
+    def __init__(self, case, call: str, layers: int, partition: int):
+        import torch
+        import paged_kv_cache_463_amd as P
+        import workloads as W
+        self.P, self.torch, self.case, self.call = P, torch, case, call
+        self.partition = partition
+        dt = getattr(torch, TORCH_DT[case.dtype])
+
+        def dev(a):
+            if case.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+        k0, v0 = dev(case.k_pool), dev(case.v_pool)
+        self.kp = [k0] + [k0.clone() for _ in range(layers - 1)]
+        self.vp = [v0] + [v0.clone() for _ in range(layers - 1)]
+        self.q = dev(case.query)
+        self.kn, self.vn = dev(case.k_new), dev(case.v_new)
+        self.slots = i32(case.slot_mapping)
+        self.bt = i32(case.block_tables)
+        self.out = torch.empty_like(self.q)
+        self.layers = layers
+        if call == "prefill":
+            self.cu = i32(case.cu_q_lens)
+            self.lens = i32(case.seq_lens)
+            self.max_q = case.max_q_len
+        else:
+            self.lens = i32(case.context_lens)
+            self.mcl = max(case.max_context_len, 1)
+            need = P.splitkv_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, self.mcl, partition)
+            self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        assert self.q.dtype == dt
+
+    def scatter(self, layer: int):
+        self.P.reshape_and_cache(self.kn, self.vn, self.kp[layer], self.vp[layer], self.slots)
+
+    def attend(self, layer: int):
+        c, P = self.case, self.P
+        if self.call == "decode":
+            P.decode(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale)
+        elif self.call == "splitkv":
+            P.decode_splitkv(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale,
+                             self.mcl, self.partition, self.ws)
+        else:
+            P.prefill_chunked(self.out, self.q, self.cu, self.max_q, self.kp[layer], self.vp[layer], self.bt,
+                              self.lens, c.scale, True)
+
+
+def time_steps(r: Runner, steps: int, warmup: int):
+    """Warm up, then time exactly ``steps`` steps; HIP events bracket every attention
+    call on the launch stream."""
+    torch = r.torch
+    for i in range(warmup):
+        r.scatter(i % r.layers)
+        r.attend(i % r.layers)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer = i % r.layers
+        r.scatter(layer)
+        ev[i][0].record(stream)
+        r.attend(layer)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    return elapsed, attn_ms
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ----------------------------------------------------------------------------
+def cpu_baseline(case, call: str, r: Runner, budget_s: float):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    kp, vp = oracle.scatter(case.k_pool, case.v_pool, case.k_new, case.v_new, case.slot_mapping)
+    gpu_out = r.out.float().cpu().double().numpy()
+    order = np.random.default_rng(0).permutation(case.num_seqs)
+    t0 = time.perf_counter()
+    done, units, err = [], 0, 0.0
+    for b in order:
+        b = int(b)
+        if call == "prefill":
+            heads = list(range(case.num_q_heads))
+            ref = oracle.paged_prefill(case.query, kp, vp, case.block_tables, case.seq_lens, case.cu_q_lens,
+                                       case.scale, case.num_kv_heads, case.dtype, seqs=[b], heads=heads)
+            q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
+            err = max(err, float(np.abs(ref[q0:q1] - gpu_out[q0:q1]).max()))
+            units += q1 - q0
+        else:
+            ref = oracle.paged_decode(case.query[[b]], kp, vp, case.block_tables[[b]], case.context_lens[[b]],
+                                      case.scale, case.num_kv_heads, case.dtype)
+            err = max(err, float(np.abs(ref[0] - gpu_out[b]).max()))
+            units += 1
+        done.append(b)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    secs = time.perf_counter() - t0
+    frac = len(done) / case.num_seqs
+    unit = "query-tokens/s" if call == "prefill" else "seq-steps/s"
+    return {"value": units / secs, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {case.num_seqs} sequences ({100 * frac:.0f}% of one step), "
+                      f"all heads, fp64 NumPy, {secs:.1f} s",
+            "max_abs_err_vs_gpu": err}
+
+
+# ----------------------------------------------------------------------------
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--kernel", default=None, choices=["decode", "splitkv", "prefill"],
+                    help="attention entry point (default: the workload's)")
+    ap.add_argument("--partition", type=int, default=512, help="split-KV partition size (tokens)")
+    ap.add_argument("--layers", type=int, default=4, help="KV pool replicas rotated over steps")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-attention path here is built and timed on a single "
+              "MI355X; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+
+    gen_key, call = WORKLOADS[args.workload]
+    call = args.kernel or call
+    t_gen = time.perf_counter()
+    case = W.NAMED[gen_key]()
+    t_gen = time.perf_counter() - t_gen
+    r = Runner(case, call, args.layers, args.partition)
+    print(f"# workload {args.workload}: generated in {t_gen:.1f} s, kernel {call}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    elapsed, attn_ms = time_steps(r, args.steps, args.warmup)
+    attn_us = float(np.mean(attn_ms)) * 1e3
+    step_ms = elapsed * 1e3 / args.steps
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": case.dtype, "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)"}
+    cfg = {"workload": args.workload, "kernel": call, "block_size": 16, "num_seqs": case.num_seqs,
+           "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+           "kv_pool_replicas": args.layers}
+    if call == "prefill":
+        flops = prefill_flops(case)
+        tokens = case.num_q_tokens
+        res.update({"value": tokens * args.steps / elapsed, "unit": "query-tokens/s"})
+        achieved = flops / (attn_us * 1e-6) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+        res["prefill_causal_flops_per_step"] = flops
+        cfg.update({"prior_tokens": int(case.prior_lens[0]), "chunk_tokens": int(case.q_lens[0]), "causal": True})
+    else:
+        ab_unique = decode_bytes(case, unique=True)
+        kv_logical, kv_unique = kv_bytes(case, False), kv_bytes(case, True)
+        res.update({"value": case.num_seqs * args.steps / elapsed, "unit": "seq-steps/s"})
+        achieved = ab_unique / (attn_us * 1e-6) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+        res["kv_gb_per_s"] = {"logical": kv_logical / (attn_us * 1e-6) / 1e9,
+                              "unique": kv_unique / (attn_us * 1e-6) / 1e9}
+        res["hbm_peak_frac"] = achieved / HBM_PEAK_GBPS
+        res["algorithmic_bytes_per_launch"] = ab_unique
+        cfg.update({"context_tokens": int(case.context_lens.astype(np.int64).sum()),
+                    "max_context_len": case.max_context_len})
+        if call == "splitkv":
+            cfg["partition_size"] = args.partition
+    res["attention_us_per_launch"] = attn_us
+    res["scatter_bytes_per_step"] = scatter_bytes(case)
+    res["config"] = cfg
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(case, call, r, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
