@@ -4,20 +4,30 @@
 // from the physical blocks in place, score q·k/sqrt(d), softmax, weight V).
 //
 // Work mapping (one workgroup = one (sequence, kv head), or one token partition
-// of it in the split-KV variant; W waves split the workgroup's blocks into
-// contiguous ranges):
+// of it in the split-KV variant; its W waves take the blocks round-robin, so
+// every wave of a long sequence has the same number of blocks to walk; grid
+// rows take the sequences longest first):
 //   * A token row of one head is D*e bytes (256 B for 16-bit D=128 or fp32 D=64).
 //     LPR = D*e/16 lanes cover a row with one 16-byte load each; a wave covers
 //     ROWS = 64/LPR rows per load, so a 16-token block is TPL = 16/ROWS loads of
-//     K and TPL of V per lane, all 16-byte, each row segment fully used.
+//     K and TPL of V per lane, each 16-byte and each row segment fully used.
 //   * The G query heads of the group share every K/V row: each lane keeps its
-//     16-byte slice of all G query vectors in registers and computes G partial
-//     dot products per row (packed dot2 for 16-bit types), reduced across the
-//     LPR lanes of the row with DPP (no LDS).
-//   * Online softmax with a wave-uniform reference max per head: scores are
-//     kept in log2 units (scale*log2 e folded in), p = 2^(s - m_ref). m_ref only
-//     moves when some score exceeds it by more than 8 (ballot, uniform branch),
-//     which bounds p by 256 and makes the rescale of the accumulators rare. The
+//     16-byte slice of all G query vectors in registers and forms G partial dot
+//     products per row (packed dot2 for 16-bit types).
+//   * Reduce-scatter instead of G all-reductions: the G partials of a row are
+//     summed over the row's LPR lanes with a DPP butterfly in which every stage
+//     keeps half of the heads and hands the other half to the partner lane, so
+//     the G full sums cost G-1 exchanges (plus the plain stages once one head is
+//     left) instead of G*log2(LPR). Afterwards lane c of a row owns the score of
+//     one head, owner(c); the lane order of the heads is a fixed linear (XOR)
+//     map of c chosen so that every DPP partner pattern lines up. Softmax
+//     bookkeeping (one exp, one running sum) is then done once per (token, head)
+//     instead of once per lane, and an all-gather through the same butterfly
+//     hands every lane the G probabilities it needs for its P·V columns.
+//   * Online softmax with a wave-uniform reference max per head: scores are in
+//     log2 units (scale*log2 e folded in), p = 2^(s - m_ref). m_ref only moves
+//     when some score exceeds it by more than 8 (ballot, uniform branch), which
+//     bounds p by 256 and makes the rescale of the accumulators rare. The
 //     softmax is unchanged by the choice of reference, which cancels in o/l.
 //   * Every lane accumulates p*V for its own columns and tokens; rows are
 //     summed once at the end, then waves are merged through LDS with the usual
@@ -25,8 +35,8 @@
 //   * Masking: only the last block of a sequence can hold dead rows (they may
 //     hold stale NaN); their scores become -inf and their V slices are zeroed
 //     before use, so 0 * NaN never happens.
-//   * Block ids are wave-uniform (scalar loads); the next block's K/V loads are
-//     issued before the current block is computed.
+//   * Block ids are wave-uniform (scalar loads, read a step ahead); two register
+//     buffers keep the next block's K/V loads in flight while a block is computed.
 //
 // Split-KV: workgroup (kv head, sequence, partition) covers logical tokens
 // [partition_size*p, partition_size*(p+1)) and writes, per query head, the
@@ -37,11 +47,197 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_SPLITKV_WAVES
+#define PA_SPLITKV_WAVES 4
+#endif
+
 namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units: p <= 2^8 between rescales
-constexpr int kDecodeWaves = 4;
+
+// ---------------------------------------------------------------------------
+// Butterfly over the LPR lanes of a row. Stage S exchanges with partner
+// lane c ^ PI_S, PI = {1, 2, 7, 15, 16} (quad perms, half-row mirror, row
+// mirror, then a cross-row swap for 32-lane rows).
+// ---------------------------------------------------------------------------
+template <int S>
+__device__ __forceinline__ float xchg(float v) {
+  if constexpr (S == 1) return dpp_f<0xB1>(v);
+  else if constexpr (S == 2) return dpp_f<0x4E>(v);
+  else if constexpr (S == 3) return dpp_f<0x141>(v);
+  else if constexpr (S == 4) return dpp_f<0x140>(v);
+  else return __shfl_xor(v, 16);
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// Head owned by lane c of a row after the reduce-scatter. Position i of a
+// lane's G-vector holds head i ^ owner(c). Stage S (S <= log2 G) splits n =
+// G >> (S-1) values in halves, so the partner's position i + n/2 must name the
+// same head as the lane's position i: owner(c ^ PI_S) = owner(c) ^ n/2. Stages
+// past log2 G are plain sums and need owner(c ^ PI_S) = owner(c). With owner
+// linear over the bits of c (bit b contributes M_b), these conditions fix M.
+template <int G>
+struct HeadMap {
+  static constexpr int mu(int s) { return G >> s; }
+  static constexpr int M0 = mu(1);
+  static constexpr int M1 = mu(2);
+  static constexpr int M2 = mu(3) ^ mu(1) ^ mu(2);
+  static constexpr int M3 = mu(4) ^ mu(3);
+  static constexpr int M4 = mu(5);
+  static __device__ __forceinline__ int owner(int c) {
+    return ((c & 1) ? M0 : 0) ^ ((c & 2) ? M1 : 0) ^ ((c & 4) ? M2 : 0) ^ ((c & 8) ? M3 : 0) ^
+           ((c & 16) ? M4 : 0);
+  }
+};
+
+template <int G, int LPR, int S = 1>
+__device__ __forceinline__ void reduce_scatter(float* v) {
+  if constexpr ((1 << (S - 1)) < LPR) {
+    constexpr int n = G >> (S - 1);
+    if constexpr (n >= 2) {
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) v[i] += xchg<S>(v[i + n / 2]);
+    } else {
+      v[0] += xchg<S>(v[0]);
+    }
+    reduce_scatter<G, LPR, S + 1>(v);
+  }
+}
+
+// Inverse of the scatter stages: from v[0] (the owned head) to all G positions.
+template <int G, int S = ilog2(G)>
+__device__ __forceinline__ void all_gather(float* v) {
+  if constexpr (S >= 1) {
+    constexpr int n = G >> (S - 1);
+#pragma unroll
+    for (int i = n / 2; i < n; ++i) v[i] = xchg<S>(v[i - n / 2]);
+    all_gather<G, S - 1>(v);
+  }
+}
+
+// Dot product of two 16-byte vectors, 16-bit types: the first dot2 of the chain
+// is the VOP3P form with an inline zero accumulator, the rest accumulate.
+template <DT dt>
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (dt == DT::BF16)
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+template <DT dt>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
+  if constexpr (dt == DT::BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, a), __builtin_bit_cast(bf162v, b), acc,
+                                          false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), acc, false);
+}
+
+template <DT dt>
+__device__ __forceinline__ float row_dot(const u32x4& a, const u32x4& b) {
+  if constexpr (dt == DT::F32) {
+    return dot16<dt>(a, b, 0.f);
+  } else {
+    const uint32_t a0 = a[0], b0 = b[0], a1 = a[1], b1 = b[1], a2 = a[2], b2 = b[2], a3 = a[3], b3 = b[3];
+    float acc = dot2_first<dt>(a0, b0);
+    acc = dot2_acc<dt>(a1, b1, acc);
+    acc = dot2_acc<dt>(a2, b2, acc);
+    return dot2_acc<dt>(a3, b3, acc);
+  }
+}
+
+// Two fp32 values rounded (to nearest even) into one dword of the 16-bit type.
+template <DT dt>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  if constexpr (dt == DT::BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf162v));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2v));
+}
+
+// 1.0 in both halves of a dword of the 16-bit type (sum of a packed pair by dot2)
+template <DT dt>
+constexpr uint32_t kOnes2 = dt == DT::BF16 ? 0x3F803F80u : 0x3C003C00u;
+
+// Longest-first dispatch. Workgroups are launched in grid order and a long
+// sequence that starts late leaves the chip idle at the end, so grid row r
+// takes the sequence of rank r in descending length (ties by index). Every
+// workgroup computes the same ranking: lengths fall into 4 buckets per
+// octave, buckets are counted in LDS and an exclusive scan gives each bucket
+// its first rank; the members of each bucket are gathered (in any order) and
+// a sequence's rank inside its bucket is the number of members with a larger
+// key (length, then reversed index) - a pure function of the lengths, so all
+// workgroups agree and the rows form a permutation of 0..B-1. Which
+// workgroup computes a sequence does not change its result. Batches above
+// kRankMaxSeqs sequences keep grid order.
+constexpr int kBuckets = 128;
+constexpr int kRankMaxSeqs = 1024;
+
+__device__ __forceinline__ int length_bucket(int L) {
+  if (L <= 0) return kBuckets - 1;
+  const int e = 31 - __clz(L);                                   // floor(log2 L)
+  const int m = (e >= 2 ? (L >> (e - 2)) : (L << (2 - e))) & 3;  // next two bits
+  return kBuckets - 1 - min(4 * e + m, kBuckets - 1);            // longer: earlier
+}
+
+__device__ __forceinline__ int rank_key(int L, int t) {          // unique for t < 1024
+  return (min(max(L, 0), (1 << 21) - 1) << 10) | (1023 - t);
+}
+
+template <int NT>
+__device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r) {
+  static_assert(NT >= kBuckets / 2, "one scan wave covers the buckets");
+  if (B > kRankMaxSeqs) return r;
+  __shared__ int s_base[kBuckets];
+  __shared__ int s_cur[kBuckets];
+  __shared__ int s_key[kRankMaxSeqs];
+  __shared__ int s_pick;
+  for (int i = threadIdx.x; i < kBuckets; i += NT) s_cur[i] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) atomicAdd(&s_cur[length_bucket(lens[t])], 1);
+  __syncthreads();
+  if (threadIdx.x < 64) {                                        // exclusive scan, 2 buckets a lane
+    const int l = threadIdx.x;
+    const int c0 = s_cur[2 * l], c1 = s_cur[2 * l + 1];
+    int inc = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (l >= o) inc += y;
+    }
+    const int exc = inc - c0 - c1;
+    s_base[2 * l] = exc;
+    s_base[2 * l + 1] = exc + c0;
+    s_cur[2 * l] = exc;
+    s_cur[2 * l + 1] = exc + c0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) {                    // gather bucket members
+    const int L = lens[t];
+    s_key[atomicAdd(&s_cur[length_bucket(L)], 1)] = rank_key(L, t);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) {
+    const int L = lens[t];
+    const int k = length_bucket(L), key = rank_key(L, t);
+    const int lo = s_base[k], hi = s_cur[k];
+    int rank = lo;
+    for (int j = lo; j < hi; ++j) rank += s_key[j] > key;
+    if (rank == r) s_pick = t;
+  }
+  __syncthreads();
+  return s_pick;
+}
 
 template <DT dt, int D, int G, int W, bool SPLIT>
 __global__ __launch_bounds__(64 * W)
@@ -52,17 +248,22 @@ void decode_kernel(DecodeParams p) {
   constexpr int ROWS = 64 / LPR;            // rows per wave load
   constexpr int TPL = kBlockSize / ROWS;    // tokens per lane per block
   static_assert(LPR >= 8 && LPR <= 32 && TPL >= 1, "unsupported head_dim/dtype");
+  static_assert(G <= LPR, "group larger than a row of lanes");
+  using HM = HeadMap<G>;
 
   __shared__ float s_acc[W][G][D];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // block walk (table reads, addresses, loop bounds) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR;
   const int c = lane % LPR;
+  const int own = HM::owner(c);
   const int g = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
   const int part = SPLIT ? (int)blockIdx.z : 0;
   const int hq0 = g * G;
 
@@ -74,17 +275,14 @@ void decode_kernel(DecodeParams p) {
     if (lo >= nblk) return;                 // whole workgroup: partition past the end
     hi = min(nblk, lo + p.partition_blocks);
   }
-  const int per = (hi - lo + W - 1) / W;
-  const int my_lo = lo + wave * per;
-  const int my_hi = min(hi, my_lo + per);
 
-  // this lane's 16-byte slice of the G query vectors
+  // this lane's 16-byte slice of the G query vectors, position i = head i ^ own
   u32x4 q[G];
   {
     const char* qb = static_cast<const char*>(p.query) +
                      (((int64_t)b * p.num_q_heads + hq0) * D + c * EPL) * E;
 #pragma unroll
-    for (int h = 0; h < G; ++h) q[h] = load16(qb + (int64_t)h * D * E);
+    for (int i = 0; i < G; ++i) q[i] = load16(qb + (int64_t)(i ^ own) * D * E);
   }
   // byte offsets of this lane's rows inside a physical block
   uint32_t off[TPL];
@@ -97,21 +295,23 @@ void decode_kernel(DecodeParams p) {
   const char* kc = static_cast<const char*>(p.k_cache);
   const char* vc = static_cast<const char*>(p.v_cache);
 
-  float m_ref[G], l[G], acc[G][EPL];
+  // softmax state of the owned head; accumulators by position
+  float m_ref = -INFINITY, l = 0.f;
+  float acc[G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_ref[h] = -INFINITY;
-    l[h] = 0.f;
+  for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
 
-  u32x4 kcur[TPL], vcur[TPL], knxt[TPL], vnxt[TPL];
-  bool ok_cur = true, ok_nxt = true;
-
-  auto fetch = [&](int i, u32x4* kd, u32x4* vd, bool& ok) {
-    int bid = tbl[i];
-    ok = (bid >= 0) && (bid < p.num_blocks);
+  // block id of logical block i (scalar load); ids are read two steps ahead of
+  // their K/V loads so the dependent table lookup never stalls a block. Past
+  // the end the last block is named again: the prefetch below is issued
+  // unconditionally (a conditional load would make the compiler's wait counts
+  // drain the prefetch of every block), and re-reading the block a wave has
+  // just read is an L2 hit.
+  auto block_id = [&](int i) -> int { return tbl[min(i, hi - 1)]; };
+  auto fetch = [&](int bid, u32x4* kd, u32x4* vd) -> bool {
+    const bool ok = (bid >= 0) && (bid < p.num_blocks);
     bid = ok ? bid : 0;                      // never address outside the pool
     const char* kb = kc + (int64_t)bid * p.block_stride_bytes;
     const char* vb = vc + (int64_t)bid * p.block_stride_bytes;
@@ -119,87 +319,133 @@ void decode_kernel(DecodeParams p) {
     for (int j = 0; j < TPL; ++j) kd[j] = load16(kb + off[j]);
 #pragma unroll
     for (int j = 0; j < TPL; ++j) vd[j] = load16(vb + off[j]);
+    return ok;
   };
 
-  if (my_lo < my_hi) fetch(my_lo, kcur, vcur, ok_cur);
-  for (int i = my_lo; i < my_hi; ++i) {
-    if (i + 1 < my_hi) fetch(i + 1, knxt, vnxt, ok_nxt);
-
-    float s[TPL][G];
+  auto process = [&](int i, u32x4* kb, u32x4* vb, bool ok) {
+    float x[TPL];
 #pragma unroll
-    for (int j = 0; j < TPL; ++j)
+    for (int j = 0; j < TPL; ++j) {
+      float v[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[j][h] = group_sum<LPR>(dot16<dt>(q[h], kcur[j], 0.f)) * sl2;
-
+      for (int h = 0; h < G; ++h) v[h] = row_dot<dt>(q[h], kb[j]);
+      reduce_scatter<G, LPR>(v);
+      x[j] = v[0] * sl2;
+    }
     const int tok0 = i * kBlockSize;
-    if (!ok_cur || tok0 + kBlockSize > L) {  // uniform: only a sequence's last block
+    if (!ok || tok0 + kBlockSize > L) {      // uniform: only a sequence's last block
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
-        if (!ok_cur || tok0 + r + ROWS * j >= L) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[j][h] = -INFINITY;
-          vcur[j] = u32x4{0u, 0u, 0u, 0u};
+        if (!ok || tok0 + r + ROWS * j >= L) {
+          x[j] = -INFINITY;
+          vb[j] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
 
     bool need = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < TPL; ++j) need |= s[j][h] > m_ref[h] + kRescaleSlack;
+    for (int j = 0; j < TPL; ++j) need |= x[j] > m_ref + kRescaleSlack;
     if (__any(need)) {
+      float mx = x[0];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = s[0][h];
+      for (int j = 1; j < TPL; ++j) mx = fmaxf(mx, x[j]);
 #pragma unroll
-        for (int j = 1; j < TPL; ++j) mx = fmaxf(mx, s[j][h]);
-        const float mn = fmaxf(m_ref[h], wave_max(mx));
-        const float corr = (m_ref[h] == -INFINITY) ? 0.f : fast_exp2(m_ref[h] - mn);
-        l[h] *= corr;
+      for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float mn = fmaxf(m_ref, mx);
+      float cg[G];
+      cg[0] = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mn);
+      l *= cg[0];
+      m_ref = mn;
+      all_gather<G>(cg);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
-        m_ref[h] = mn;
-      }
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= cg[h];
     }
 
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    if constexpr (dt == DT::F32) {
 #pragma unroll
-    for (int j = 0; j < TPL; ++j) {
-      float vf[EPL];
-      unpack<dt>(vcur[j], vf);
+      for (int j = 0; j < TPL; ++j) {
+        float pg[G];
+        pg[0] = fast_exp2(x[j] - mu);
+        l += pg[0];
+        all_gather<G>(pg);
+        float vf[EPL];
+        unpack<dt>(vb[j], vf);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pj = fast_exp2(s[j][h] - m_ref[h]);
-        l[h] += pj;
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pg[h], vf[e], acc[h][e]);
+      }
+    } else {
+      // 16-bit types: P·V on packed dot2 over the lane's token pairs (j, j+1).
+      // The pair's probabilities are rounded to the input type once, in the
+      // owning lane; the normaliser sums the same rounded values, so the
+      // output stays a convex combination of the V rows.
+#pragma unroll
+      for (int j = 0; j < TPL; j += 2) {
+        float pg[G];
+        const uint32_t pk = pack2<dt>(fast_exp2(x[j] - mu), fast_exp2(x[j + 1] - mu));
+        l = dot2_acc<dt>(pk, kOnes2<dt>, l);
+        pg[0] = __uint_as_float(pk);
+        all_gather<G>(pg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t v0 = vb[j][i], v1 = vb[j + 1][i];
+          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);   // column 2i of both tokens
+          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);   // column 2i+1
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t ph = __float_as_uint(pg[h]);
+            acc[h][2 * i] = dot2_acc<dt>(ph, lo, acc[h][2 * i]);
+            acc[h][2 * i + 1] = dot2_acc<dt>(ph, hi, acc[h][2 * i + 1]);
+          }
+        }
       }
     }
+  };
 
-#pragma unroll
-    for (int j = 0; j < TPL; ++j) { kcur[j] = knxt[j]; vcur[j] = vnxt[j]; }
-    ok_cur = ok_nxt;
+  // blocks lo + wave, lo + wave + W, ... ; two register buffers
+  u32x4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
+  const int first = lo + wave;
+  if (first < hi) {
+    // both buffers in flight before the first block is computed; each buffer is
+    // refilled with the block two steps ahead as soon as it has been consumed
+    bool okA = fetch(block_id(first), kA, vA);
+    bool okB = fetch(block_id(first + W), kB, vB);
+    int bid = block_id(first + 2 * W);
+    for (int i = first;; i += 2 * W) {
+      process(i, kA, vA, okA);
+      okA = fetch(bid, kA, vA);
+      bid = block_id(i + 3 * W);
+      if (i + W >= hi) break;
+      process(i + W, kB, vB, okB);
+      okB = fetch(bid, kB, vB);
+      bid = block_id(i + 4 * W);
+      if (i + 2 * W >= hi) break;
+    }
   }
 
-  // sum the ROWS row-streams of the wave (all lanes of a row hold equal l)
+  // sum the ROWS row-streams of the wave (lanes of one c share the head order)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int o = LPR; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o);
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      l[h] += __shfl_xor(l[h], o);
+    for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-    }
   }
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][c * EPL + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) { s_m[wave][h] = m_ref[h]; s_l[wave][h] = l[h]; }
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h ^ own][c * EPL + e] = acc[h][e];
+    if (c < G) {                            // lanes 0..G-1 own distinct heads
+      s_m[wave][own] = m_ref;
+      s_l[wave][own] = l;
+    }
   }
   __syncthreads();
 
@@ -261,16 +507,24 @@ void splitkv_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+// Waves per workgroup; fp32 with head_dim 128 holds twice the bytes per lane
+// and stays at 4 waves so that its registers fit without spilling.
+template <DT dt, int D, bool SPLIT>
+constexpr int decode_waves() {
+  return (dt == DT::F32 && D == 128) ? 4 : (SPLIT ? PA_SPLITKV_WAVES : PA_DECODE_WAVES);
+}
+
 template <DT dt, int D, bool SPLIT>
 static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+  constexpr int W = decode_waves<dt, D, SPLIT>();
   const int G = p.num_q_heads / p.num_kv_heads;
   dim3 grid(p.num_kv_heads, p.num_seqs, SPLIT ? p.max_parts : 1);
-  dim3 block(64 * kDecodeWaves);
+  dim3 block(64 * W);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, kDecodeWaves, SPLIT>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<dt, D, 2, kDecodeWaves, SPLIT>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<dt, D, 4, kDecodeWaves, SPLIT>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<dt, D, 8, kDecodeWaves, SPLIT>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<dt, D, 2, W, SPLIT>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<dt, D, 4, W, SPLIT>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<dt, D, 8, W, SPLIT>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
