@@ -33,9 +33,15 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file extra flags. The prefill kernel runs with the IEEE mode bit off and
+# no NaN operands assumed: masked scores are -inf selects and every key a tile
+# reads is a cached row, so max() needs no quieting of its inputs.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -7,30 +7,38 @@
 // q_len positions, query i sits at absolute position seq_len - q_len + i and
 // sees keys 0 .. that position.
 //
-// Tiling (one workgroup of 4 waves):
-//   * a workgroup owns one (sequence, kv head) and 256 "columns" = (query
-//     position, query head of the group) pairs: BQ = 256/G consecutive chunk
+// Tiling (one workgroup of 4 waves, two workgroups per CU):
+//   * a workgroup owns one (sequence, kv head) and 128 "columns" = (query
+//     position, query head of the group) pairs: BQ = 128/G consecutive chunk
 //     positions for all G heads of the group, so every K/V tile it stages is
-//     shared by G heads. Wave w owns columns 64w .. 64w+63 as two 32-column
-//     N-tiles.
+//     shared by G heads. Wave w owns columns 32w .. 32w+31, one 32-wide MFMA
+//     N-tile, which keeps its accumulators, scores and query operand within
+//     half the register file (two waves per SIMD: one wave's softmax overlaps
+//     the other's matrix work).
 //   * keys advance in tiles of 64 (four 16-token blocks gathered through the
-//     block table). K is staged in LDS row-major [key][d] (pitch D+8 elements),
-//     V transposed [d][key] (pitch 68 elements) so both MFMA operands read
-//     16-byte / 8-byte contiguous runs without bank conflicts on the K side.
-//     Two LDS stages: tile t+1 is fetched into registers while tile t is
-//     computed, then written to the other stage; one barrier per tile.
+//     block table). K is staged in LDS row-major [key][d] (pitch D+8
+//     elements), V transposed [d][key] (pitch 68 elements) so both MFMA
+//     operands read contiguous 16-byte / 8-byte runs; the V thread mapping
+//     makes the transposed writes bank-conflict free. Software pipeline: while
+//     the VALU turns the scores of tile t into P, the matrix cores already
+//     compute the scores of tile t+1; K runs one tile ahead of V through two
+//     LDS buffers each, fetched into registers a tile ahead; one barrier per
+//     tile.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q from
 //     registers, loaded once). In this layout a lane holds 16 keys of ONE
 //     query column, so the softmax max/sum are in-lane plus one exchange with
 //     lane ^ 32.
 //   * online softmax in log2 units with a per-column reference max that only
 //     moves when a score exceeds it by more than 8; P is rounded to the input
-//     type and fed as the B operand of O^T += V^T P^T. The key order inside
-//     each 16-key MFMA step follows the S^T register order; the V^T reads use
-//     the same order, so the contraction is unchanged.
-//   * masking: keys past the causal limit get score -inf (select, never a
+//     type, summed for the normaliser from the rounded values (packed dot2
+//     against ones), and fed as the B operand of O^T += V^T P^T. The key order
+//     inside each 16-key MFMA step follows the S^T register order; the V^T
+//     reads use the same order, so the contraction is unchanged.
+//   * masking (only in tiles that reach the causal diagonal or the end of the
+//     keys): keys past the causal limit get score -inf (select, never a
 //     multiply), and V rows of keys outside [0, kend) are written to LDS as
-//     zeros, so stale NaN in unused slots never meets P = 0.
+//     zeros, so stale NaN in unused slots never meets P = 0. Columns past the
+//     chunk's end carry a zero query and are never stored.
 //   * XCD-aware order: workgroups of one (sequence, kv head) share its K/V
 //     through L2, so they are placed on the same XCD (linear id i runs on XCD
 //     i % 8); within a pair the tiles with the most keys start first.
@@ -44,15 +52,17 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kCols = 256;                   // columns per workgroup
+constexpr int kCols = 32 * kWaves;           // columns per workgroup
 constexpr int kBK = 64;                      // keys per tile
-constexpr int kVtPitch = kBK + 4;            // V^T row pitch (elements)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <DT dt> struct Mfma;
@@ -61,14 +71,26 @@ template <> struct Mfma<DT::BF16> {
   static __device__ __forceinline__ f32x16 run(const vec& a, const vec& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint16_t bits(float x) { return to_bf16_bits(x); }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {   // acc + lo + hi
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
 };
 template <> struct Mfma<DT::F16> {
   typedef f16x8 vec;
   static __device__ __forceinline__ f32x16 run(const vec& a, const vec& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint16_t bits(float x) { return to_f16_bits(x); }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), __builtin_bit_cast(f16x2, 0x3C003C00u), acc,
+                                  false);
+  }
 };
 
 template <typename V>
@@ -77,26 +99,31 @@ __device__ __forceinline__ V as_vec(const u32x4& u) { return __builtin_bit_cast(
 }  // namespace
 
 template <DT dt, int D, int G>
-__global__ __launch_bounds__(64 * kWaves)
+__global__ __launch_bounds__(64 * kWaves, 2)
 void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   using M = Mfma<dt>;
   using vec = typename M::vec;
   constexpr int BQ = kCols / G;              // chunk positions per workgroup
-  constexpr int KPitch = D + 8;              // K row pitch (elements)
   constexpr int CH = D * 2 / 16;             // 16-byte chunks per K/V row
-  constexpr int KPT = kBK * CH / (64 * kWaves);   // keys per thread per tile (2 or 4)
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
   constexpr int MD = D / 32;                 // 32-row tiles of head_dim in O^T
-  static_assert(KPT == 2 || KPT == 4, "tile mapping");
+  constexpr int RB = D * 2;                  // bytes of one K/V row in LDS (unpadded, swizzled)
+  constexpr int NI = kBlockSize * RB / 1024; // 1 KB DMA instructions per wave per tile (4 or 2)
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBK * KPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * kVtPitch];
+  // K and V tiles, row-major, two buffers each, filled by direct global->LDS
+  // loads. 16-byte granule c of row r sits at position c ^ kswz(r) (K) or
+  // c ^ vswz(r) (V), chosen (by bank-conflict counts) so that the 16-byte K
+  // reads of 16 consecutive rows and the transposing 8-byte V reads of two
+  // 16-lane groups over 4 consecutive rows hit distinct banks.
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kBK * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kBK * RB];
 
   // ---- which (sequence, kv head, tile) -----------------------------------
   const int npairs = p.num_seqs * p.num_kv_heads;
   int pair, tile;
   {
-    const int lin = blockIdx.x;
+    const int lin = __builtin_amdgcn_workgroup_id_x();   // builtins: this unit is built with the
+                                                        // IEEE bit off, which keeps library calls out of line
     if (xcd_mapped) {                        // all tiles of a pair on one XCD
       const int xcd = lin & 7, k = lin >> 3;
       pair = xcd + 8 * (k / tiles_per_pair);
@@ -120,225 +147,280 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   const int nkt = (kend + kBK - 1) / kBK;
   const int nblk_valid = min((kend + kBlockSize - 1) / kBlockSize, p.block_table_stride);
 
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;                  // which half of the 32x32 operand
   const int col = lane & 31;
 
-  // ---- this lane's query columns (two N-tiles) ---------------------------
-  int qpos[2], pabs[2];
-  bool cvalid[2];
-  vec qreg[2][DS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int c = (2 * wave + nt) * 32 + col;
-    const int hl = c / BQ;
-    qpos[nt] = q0 + c % BQ;
-    cvalid[nt] = qpos[nt] < qlen;
-    pabs[nt] = cvalid[nt] ? s0 + qpos[nt] : -1;
+  // ---- this lane's query column (one N-tile per wave) ---------------------
+  const int cidx = wave * 32 + col;
+  const int hl = cidx / BQ;
+  const int qpos = q0 + cidx % BQ;
+  const bool cvalid = qpos < qlen;
+  const int pabs = cvalid ? s0 + qpos : -1;
+  vec qreg[DS];
+  {
     const char* qrow = static_cast<const char*>(p.query) +
-                       (((int64_t)(cu0 + (cvalid[nt] ? qpos[nt] : 0)) * p.num_q_heads + g * G + hl) * D) * 2;
+                       (((int64_t)(cu0 + (cvalid ? qpos : 0)) * p.num_q_heads + g * G + hl) * D) * 2;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      u32x4 u = cvalid[nt] ? load16(qrow + (ds * 16 + 8 * hi) * 2) : u32x4{0u, 0u, 0u, 0u};
-      qreg[nt][ds] = as_vec<vec>(u);
+      u32x4 u = cvalid ? load16(qrow + (ds * 16 + 8 * hi) * 2) : u32x4{0u, 0u, 0u, 0u};
+      qreg[ds] = as_vec<vec>(u);
     }
   }
 
-  // ---- cooperative tile fetch: thread -> (key group, 16-byte chunk) -------
-  const int dchunk = tid % CH;
-  const int kg = tid / CH;                   // keys kg*KPT .. kg*KPT+KPT-1 of the tile
-  const int32_t* tbl = p.block_tables + (int64_t)b * p.block_table_stride;
+  // ---- tile loads: direct global -> LDS ----------------------------------
+  // Wave w loads logical block 4t+w of tile t (16 keys): DMA instruction n of a
+  // wave writes 1 KB at LDS offset 16w*RB + 1024n, 16 bytes per lane, and each
+  // lane fetches the global granule whose swizzled position that is.
+  // the table is read-only for the kernel's lifetime: read it through the
+  // constant address space so the uniform lookups stay scalar loads
+  const __attribute__((address_space(4))) int32_t* tbl =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.block_table_stride);
   const char* kc = static_cast<const char*>(p.k_cache);
   const char* vc = static_cast<const char*>(p.v_cache);
-  const int64_t row_bytes = (int64_t)p.num_kv_heads * D * 2;
-  u32x4 kreg[KPT], vreg[KPT];
-
-  auto fetch = [&](int t) {
+  const int64_t prow = (int64_t)p.num_kv_heads * D * 2;     // bytes of one pool row (all kv heads)
+  auto kswz = [](int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return RB == 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  uint32_t k_src[NI], v_src[NI];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = t * kBK + kg * KPT + i;
-      const int blk = key / kBlockSize;
-      int bid = blk < nblk_valid ? tbl[blk] : 0;
-      bid = (bid >= 0 && bid < p.num_blocks) ? bid : 0;
-      const int64_t off = (int64_t)bid * p.block_stride_bytes + (key % kBlockSize) * row_bytes +
-                          (int64_t)g * D * 2 + dchunk * 16;
-      kreg[i] = load16(kc + off);
-      vreg[i] = load16(vc + off);
-    }
+  for (int n = 0; n < NI; ++n) {
+    const int r = (n * 1024 + 16 * lane) / RB;               // row inside the wave's block
+    const int gp = lane % (RB / 16);                         // granule position inside the row
+    const uint32_t row_off = (uint32_t)(r * prow + (int64_t)g * D * 2);
+    k_src[n] = row_off + ((gp ^ kswz(r)) << 4);     // the swizzles use the row's low 4 bits only
+    v_src[n] = row_off + ((gp ^ vswz(r)) << 4);
+  }
+  // table entry of this wave's logical block in tile t (scalar: the index is
+  // uniform), and the byte offset of its physical block; blocks past the
+  // visible keys read block 0
+  auto entry = [&](int t) -> int {
+    return tbl[min(min(t, nkt - 1) * (kBK / kBlockSize) + wave, nblk_valid - 1)];
   };
-  auto stage = [&](int t, int buf) {
+  auto block_base = [&](int t, int bid) -> int64_t {
+    const int blk = min(t, nkt - 1) * (kBK / kBlockSize) + wave;
+    bid = (blk < nblk_valid && bid >= 0 && bid < p.num_blocks) ? bid : 0;
+    return (int64_t)bid * p.block_stride_bytes;
+  };
+  // One direct global -> LDS load of 16 bytes per lane: M0 holds the LDS
+  // destination of lane 0 (lane i writes 16 bytes further per lane), the
+  // global address is a scalar block base plus a 32-bit lane offset. Issued as
+  // inline assembly: the completion of these loads is waited for explicitly
+  // (s_waitcnt vmcnt(0) and a barrier, once per tile), and the buffers read
+  // while they are in flight are never their destinations.
+  auto lds_load16 = [&](const char* base, uint32_t off, const uint8_t* lds_dst) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
+  };
+  // issue the loads of K tile tk (table entry kbid) into sK[kb] and V tile tv
+  // (entry vbid) into sV[vb]; tiles past the end re-read the last tile, so
+  // every wave issues the same loads
+  auto dma = [&](int tk, int kbid, int kb, int tv, int vbid, int vb) {
+    const char* ks = kc + block_base(tk, kbid);
+    const char* vs = vc + block_base(tv, vbid);
+    const uint8_t* kd = &sK[kb][wave * kBlockSize * RB];
+    const uint8_t* vd = &sV[vb][wave * kBlockSize * RB];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = kg * KPT + i;
-      *reinterpret_cast<u32x4*>(&sK[buf][key * KPitch + dchunk * 8]) = kreg[i];
-    }
-    // V^T: KPT consecutive keys of one column packed together; keys outside
-    // [0, kend) are zeroed so stale slots never reach the MFMA
+    for (int n = 0; n < NI; ++n) lds_load16(ks, k_src[n], kd + n * 1024);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = t * kBK + kg * KPT + i;
-      if (key >= kend) vreg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int n = 0; n < NI; ++n) lds_load16(vs, v_src[n], vd + n * 1024);
+  };
+  // wait for this wave's loads; in the last V tile zero the rows of keys past
+  // kend (stale slots) in this wave's block, then make everything visible
+  auto land = [&](int tv, int vb) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tv < nkt && tv * kBK + kBK > kend) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = dchunk * 8 + e;
-      uint16_t v16[KPT];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const uint32_t w = vreg[i][e >> 1];
-        v16[i] = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFFu);
+      for (int n = 0; n < NI; ++n) {
+        const int r = (n * 1024 + 16 * lane) / RB;
+        if (tv * kBK + wave * kBlockSize + r >= kend)
+          *reinterpret_cast<u32x4*>(&sV[vb][wave * kBlockSize * RB + n * 1024 + 16 * lane]) = u32x4{0u, 0u, 0u, 0u};
       }
-      uint16_t* dst = &sVt[buf][d * kVtPitch + kg * KPT];
-      if constexpr (KPT == 4) {
-        u32x2 pk = {(uint32_t)v16[0] | ((uint32_t)v16[1] << 16), (uint32_t)v16[2] | ((uint32_t)v16[3] << 16)};
-        *reinterpret_cast<u32x2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)v16[0] | ((uint32_t)v16[1] << 16);
-      }
     }
+    __syncthreads();
   };
 
   // ---- accumulators --------------------------------------------------------
-  f32x16 o[MD][2];
+  f32x16 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[md][nt][r] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
+  float mref = -INFINITY;
+  float lsum = 0.f;
   const float sl2 = p.scale * kLog2e;
 
-  fetch(0);
-  stage(0, 0);
-  __syncthreads();
-
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) fetch(t + 1);
-    const uint16_t* K_ = sK[buf];
-    const uint16_t* Vt = sVt[buf];
-    const int key0 = t * kBK;
-
-    // S^T for 2 key sub-tiles x 2 column tiles
-    f32x16 s[2][2];
+  // Software pipeline over key tiles: iteration t computes the scores of tile
+  // t+1 on the matrix cores while the VALU turns the scores of tile t into P,
+  // then accumulates P V of tile t. K runs one tile ahead of V in LDS: during
+  // iteration t the wave reads K(t+1) and V(t) and the workgroup writes K(t+2)
+  // and V(t+1) into the other two buffers; one barrier per tile.
+  f32x16 sc[2], sn[2];                       // scores of the current / next tile
+  dma(0, entry(0), 0, 0, entry(0), 0);
+  land(0, 0);
+  dma(1, entry(1), 1, nkt, entry(nkt), 1);    // K(1); the V part re-reads tile nkt-1 into sV[1]
+  // table entries for the loads of the next iteration, read a tile ahead
+  int kbid_next = entry(2), vbid_next = entry(1);
+  {
+    const uint8_t* K0 = sK[0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const f32x16 z = {};
+      sc[kt] = z;
+      const int r = kt * 32 + col;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][nt][r] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const vec a = as_vec<vec>(*reinterpret_cast<const u32x4*>(&K_[(kt * 32 + col) * KPitch + ds * 16 + 8 * hi]));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s[kt][nt] = M::run(a, qreg[nt][ds], s[kt][nt]);
-      }
+      for (int ds = 0; ds < DS; ++ds)
+        sc[kt] = M::run(as_vec<vec>(*reinterpret_cast<const u32x4*>(&K0[r * RB + (((2 * ds + hi) ^ kswz(r)) << 4)])),
+                        qreg[ds], sc[kt]);
     }
+  }
+  land(nkt, 1);
 
-    // scale, mask, tile max per column
+  for (int t = 0; t < nkt; ++t) {
+    const int key0 = t * kBK;
+    dma(t + 2, kbid_next, t & 1, t + 1, vbid_next, (t + 1) & 1);
+
+    // scale; mask (uniform: only tiles that reach the causal diagonal or the
+    // end of the keys); tile max of the column; rare rescale
     const bool edge = (key0 + kBK > kend) || (p.causal && key0 + kBK - 1 > s0 + q0);
-    float tmax[2] = {-INFINITY, -INFINITY};
+    if (edge) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kt][nt][r] * sl2;
-          if (edge || !cvalid[nt]) {
-            const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool vis = cvalid[nt] && key < kend && (!p.causal || key <= pabs[nt]);
-            x = vis ? x : -INFINITY;
-          }
-          s[kt][nt][r] = x;
-          tmax[nt] = fmaxf(tmax[nt], x);
+          const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool vis = key < kend && (!p.causal || key <= pabs);
+          sc[kt][r] = vis ? sc[kt][r] : -INFINITY;
         }
-      }
-      tmax[nt] = fmaxf(tmax[nt], __shfl_xor(tmax[nt], 32));
     }
-    const bool need = (tmax[0] > mref[0] + kSlack) || (tmax[1] > mref[1] + kSlack);
-    if (__any(need)) {
+    float tmax = -INFINITY;                   // on raw scores (scale > 0)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mn = fmaxf(mref[nt], tmax[nt]);
-        const float corr = (mref[nt] == -INFINITY) ? 0.f : fast_exp2(mref[nt] - mn);
-        lsum[nt] *= corr;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int md = 0; md < MD; ++md)
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(sc[kt][r], sc[kt][r + 1]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;
+    if (__any(tmax > mref + kSlack)) {
+      const float mn = fmaxf(mref, tmax);
+      const float corr = (mref == -INFINITY) ? 0.f : fast_exp2(mref - mn);
+      lsum *= corr;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[md][nt][r] *= corr;
-        mref[nt] = mn;
-      }
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[md][r] *= corr;
+      mref = mn;
     }
+    const float mu = (mref == -INFINITY) ? 0.f : mref;
 
-    // P (rounded to the input type) as B operands, row sums
-    vec pb[2][2][2];                          // [kt][nt][half of the 32 keys]
+    // scores of tile t+1 (matrix cores) interleaved with P of tile t (VALU):
+    // P = 2^(s - m) rounded to the input type, normaliser from the rounded
+    // values. Step ds issues the two MFMAs of k-step ds and the exp / pack /
+    // sum of PPS pairs of scores; a scheduling barrier closes each step so the
+    // matrix and vector streams stay interleaved. The last iteration computes
+    // scores it never uses (its buffer holds an older tile).
+    u32x4 pk[2][2];                           // [kt][16-key step]: packed P pairs
+    {
+      constexpr int PPS = 16 / DS;            // score pairs per k-step
+      const uint8_t* Kn = sK[(t + 1) & 1];
+      auto kfrag = [&](int kt, int ds) {
+        const int r = kt * 32 + col;
+        return as_vec<vec>(*reinterpret_cast<const u32x4*>(&Kn[r * RB + (((2 * ds + hi) ^ kswz(r)) << 4)]));
+      };
+      vec ka[2][2];
+      ka[0][0] = kfrag(0, 0);
+      ka[0][1] = kfrag(1, 0);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float mu = (mref[nt] == -INFINITY) ? 0.f : mref[nt];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          u32x4 pk;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = fast_exp2(s[kt][nt][8 * ss + 2 * e2] - mu);
-            const float p1 = fast_exp2(s[kt][nt][8 * ss + 2 * e2 + 1] - mu);
-            lsum[nt] += p0 + p1;
-            pk[e2] = (uint32_t)M::bits(p0) | ((uint32_t)M::bits(p1) << 16);
-          }
-          pb[kt][nt][ss] = as_vec<vec>(pk);
+      for (int ds = 0; ds < DS; ++ds) {
+        if (ds + 1 < DS) {
+          ka[(ds + 1) & 1][0] = kfrag(0, ds + 1);
+          ka[(ds + 1) & 1][1] = kfrag(1, ds + 1);
         }
-      }
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const uint16_t* vrow = &Vt[(md * 32 + col) * kVtPitch];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const int kb = kt * 32 + 16 * ss + 4 * hi;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&vrow[kb]);
-          const u32x2 up = *reinterpret_cast<const u32x2*>(&vrow[kb + 8]);
-          const vec a = as_vec<vec>(u32x4{lo[0], lo[1], up[0], up[1]});
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) o[md][nt] = M::run(a, pb[kt][nt][ss], o[md][nt]);
+        if (ds == 0) {
+          const f32x16 z = {};
+          sn[0] = M::run(ka[0][0], qreg[0], z);
+          sn[1] = M::run(ka[0][1], qreg[0], z);
+        } else {
+          sn[0] = M::run(ka[ds & 1][0], qreg[ds], sn[0]);
+          sn[1] = M::run(ka[ds & 1][1], qreg[ds], sn[1]);
         }
+#pragma unroll
+        for (int j = 0; j < PPS; ++j) {
+          const int pr = ds * PPS + j;        // pair index 0..15: (kt, ss, e2)
+          const int kt = pr >> 3, ss = (pr >> 2) & 1, e2 = pr & 3;
+          const float p0 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2], sl2, -mu));
+          const float p1 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2 + 1], sl2, -mu));
+          pk[kt][ss][e2] = M::pack(p0, p1);
+          lsum = M::sum2(pk[kt][ss][e2], lsum);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    vec pb[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) pb[kt][ss] = as_vec<vec>(pk[kt][ss]);
 
-    if (t + 1 < nkt) stage(t + 1, buf ^ 1);
-    __syncthreads();
+    // O^T += V^T P^T over V(t). The A operand (32 head-dim rows x 16 keys) is
+    // read from row-major V with two transposing 8-byte reads: in each group of
+    // 16 lanes, lane 4j+q names key j of the read at columns 4q..4q+3 and lane
+    // i receives column i of the 4 named keys. Read 0 covers keys 4h..4h+3 and
+    // read 1 keys 8+4h..8+4h+3 of the 16-key step (h = lane / 32), which is the
+    // key order of the P^T operand.
+    {
+      const uint8_t* Vc = sV[t & 1];
+      const int vg = lane >> 4, vj = (lane >> 2) & 3, vq = lane & 3, vh = lane >> 5;
+      auto vfrag = [&](int md, int kt, int ss) {
+        const int d = md * 32 + 16 * (vg & 1) + 4 * vq;
+        const int key0 = kt * 32 + 16 * ss + 4 * vh + vj;
+        const int key1 = key0 + 8;
+        const uint32_t gr = (uint32_t)(d >> 3), lo8 = (uint32_t)((d & 7) << 1);
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(Vc + key0 * RB + (((gr ^ vswz(key0)) << 4) | lo8)));
+        const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(Vc + key1 * RB + (((gr ^ vswz(key1)) << 4) | lo8)));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+        return as_vec<vec>(u32x4{a0[0], a0[1], a1[0], a1[1]});
+      };
+      // step i: key step ks = i / MD of the 64 keys, output tile md = i % MD, so
+      // consecutive MFMAs accumulate into different tiles
+      constexpr int NV = MD * 4;
+      auto vstep = [&](int i) { return vfrag(i % MD, (i / MD) >> 1, (i / MD) & 1); };
+      vec va[3];
+      va[0] = vstep(0);
+      va[1] = vstep(1);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i + 2 < NV) va[(i + 2) % 3] = vstep(i + 2);
+        const int md = i % MD, ks = i / MD;
+        o[md] = M::run(va[i % 3], pb[ks >> 1][ks & 1], o[md]);
+      }
+    }
+    kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
+    vbid_next = entry(t + 2);                 // loads complete during the wait below
+    land(t + 1, (t + 1) & 1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sc[kt] = sn[kt];
   }
 
   // ---- normalise and store ------------------------------------------------
+  const float l = lsum + __shfl_xor(lsum, 32);
+  if (!cvalid) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)(cu0 + qpos) * p.num_q_heads + g * G + hl) * D;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float l = lsum[nt] + __shfl_xor(lsum[nt], 32);
-    if (!cvalid[nt]) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int c = (2 * wave + nt) * 32 + col;
-    const int hl = c / BQ;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) +
-                     ((int64_t)(cu0 + qpos[nt]) * p.num_q_heads + g * G + hl) * D;
+  for (int md = 0; md < MD; ++md) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = md * 32 + 8 * j + 4 * hi;
-        u32x2 pk;
-        pk[0] = (uint32_t)M::bits(o[md][nt][4 * j] * inv) | ((uint32_t)M::bits(o[md][nt][4 * j + 1] * inv) << 16);
-        pk[1] = (uint32_t)M::bits(o[md][nt][4 * j + 2] * inv) | ((uint32_t)M::bits(o[md][nt][4 * j + 3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(orow + d) = pk;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int d = md * 32 + 8 * j + 4 * hi;
+      u32x2 pk;
+      pk[0] = M::pack(o[md][4 * j] * inv, o[md][4 * j + 1] * inv);
+      pk[1] = M::pack(o[md][4 * j + 2] * inv, o[md][4 * j + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + d) = pk;
     }
   }
 }
