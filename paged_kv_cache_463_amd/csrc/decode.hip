@@ -38,10 +38,11 @@
 //   * Block ids are wave-uniform (scalar loads, read a step ahead); two register
 //     buffers keep the next block's K/V loads in flight while a block is computed.
 //
-// Split-KV: workgroup (kv head, sequence, partition) covers logical tokens
-// [partition_size*p, partition_size*(p+1)) and writes, per query head, the
-// unnormalised output row plus (max, normaliser) to the workspace; a second
-// kernel merges partitions by log-sum-exp.
+// Split-KV: wave w of workgroup (kv head, sequence, z) covers partition
+// p = W*z + w, logical tokens [partition_size*p, partition_size*(p+1)), on its
+// own and writes, per query head, the unnormalised output row plus (max,
+// normaliser) to the workspace; a second kernel merges partitions by
+// log-sum-exp.
 #include <math.h>
 
 #include "pa_device.h"
@@ -264,15 +265,18 @@ void decode_kernel(DecodeParams p) {
   const int own = HM::owner(c);
   const int g = blockIdx.x;
   const int b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
-  const int part = SPLIT ? (int)blockIdx.z : 0;
+  const int part = SPLIT ? (int)blockIdx.z * W + wave : 0;
   const int hq0 = g * G;
 
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
+  // single pass: the W waves share the sequence's blocks round-robin.
+  // split-KV: wave w walks partition W*z + w on its own (no merge across waves)
+  constexpr int STEP = SPLIT ? 1 : W;
   int lo = 0, hi = nblk;
   if constexpr (SPLIT) {
     lo = part * p.partition_blocks;
-    if (lo >= nblk) return;                 // whole workgroup: partition past the end
+    if (lo >= nblk) return;                 // this wave's partition lies past the end
     hi = min(nblk, lo + p.partition_blocks);
   }
 
@@ -407,24 +411,24 @@ void decode_kernel(DecodeParams p) {
     }
   };
 
-  // blocks lo + wave, lo + wave + W, ... ; two register buffers
+  // blocks first, first + STEP, ... ; two register buffers
   u32x4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
-  const int first = lo + wave;
+  const int first = SPLIT ? lo : lo + wave;
   if (first < hi) {
     // both buffers in flight before the first block is computed; each buffer is
     // refilled with the block two steps ahead as soon as it has been consumed
     bool okA = fetch(block_id(first), kA, vA);
-    bool okB = fetch(block_id(first + W), kB, vB);
-    int bid = block_id(first + 2 * W);
-    for (int i = first;; i += 2 * W) {
+    bool okB = fetch(block_id(first + STEP), kB, vB);
+    int bid = block_id(first + 2 * STEP);
+    for (int i = first;; i += 2 * STEP) {
       process(i, kA, vA, okA);
       okA = fetch(bid, kA, vA);
-      bid = block_id(i + 3 * W);
-      if (i + W >= hi) break;
-      process(i + W, kB, vB, okB);
+      bid = block_id(i + 3 * STEP);
+      if (i + STEP >= hi) break;
+      process(i + STEP, kB, vB, okB);
       okB = fetch(bid, kB, vB);
-      bid = block_id(i + 4 * W);
-      if (i + 2 * W >= hi) break;
+      bid = block_id(i + 4 * STEP);
+      if (i + 2 * STEP >= hi) break;
     }
   }
 
@@ -436,6 +440,23 @@ void decode_kernel(DecodeParams p) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+  }
+  if constexpr (SPLIT) {                    // the wave's partial goes straight to the workspace
+    if (r == 0) {
+      const int64_t row0 = (int64_t)b * p.num_q_heads + hq0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int64_t pr = (row0 + (h ^ own)) * p.max_parts + part;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) p.ws_acc[pr * D + c * EPL + e] = acc[h][e];
+      }
+      if (c < G) {                          // lanes 0..G-1 own distinct heads
+        const int64_t pr = (row0 + own) * p.max_parts + part;
+        p.ws_ml[2 * pr] = m_ref;
+        p.ws_ml[2 * pr + 1] = l;
+      }
+    }
+    return;
   }
   if (r == 0) {
 #pragma unroll
@@ -463,13 +484,7 @@ void decode_kernel(DecodeParams p) {
       den = fmaf(sc, s_l[w][h], den);
     }
     const int64_t row = (int64_t)b * p.num_q_heads + hq0 + h;
-    if constexpr (!SPLIT) {
-      store_elem<dt>(p.out, row * D + d, den > 0.f ? num / den : 0.f);
-    } else {
-      const int64_t pr = row * p.max_parts + part;
-      p.ws_acc[pr * D + d] = num;
-      if (d == 0) { p.ws_ml[2 * pr] = M; p.ws_ml[2 * pr + 1] = den; }
-    }
+    store_elem<dt>(p.out, row * D + d, den > 0.f ? num / den : 0.f);
   }
 }
 
@@ -518,7 +533,7 @@ template <DT dt, int D, bool SPLIT>
 static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   constexpr int W = decode_waves<dt, D, SPLIT>();
   const int G = p.num_q_heads / p.num_kv_heads;
-  dim3 grid(p.num_kv_heads, p.num_seqs, SPLIT ? p.max_parts : 1);
+  dim3 grid(p.num_kv_heads, p.num_seqs, SPLIT ? (p.max_parts + W - 1) / W : 1);
   dim3 block(64 * W);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT>), grid, block, 0, s, p); break;
