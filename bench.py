@@ -29,6 +29,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV GB/s, % of MI355X HBM peak, seq-steps/s"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "paged_kv_cache_463_amd", "csrc")
+# sources that define each attention launch (a change to any of them makes a
+# stored HBM-traffic measurement stale)
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "pa_device.h", "pa_launch.h"],
+    "splitkv": ["decode.hip", "pa_device.h", "pa_launch.h"],
+    "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h"],
+}
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6    # dense, 256 CUs at 2.4 GHz
 TORCH_DT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
@@ -85,6 +94,31 @@ def prefill_flops(case) -> int:
         pos = L - ql + np.arange(ql)
         pairs += int((pos + 1).sum())
     return 4 * case.head_dim * case.num_q_heads * pairs
+
+
+def kernel_source_sha256(call: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[call] + ["../build.py"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, call: str, partition: int):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when there is none or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{call}_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256(call):
+        return None
+    if call == "splitkv" and rec.get("partition_size") != partition:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 # ----------------------------------------------------------------------------
@@ -264,7 +298,8 @@ def main(argv=None) -> int:
         res.update({"value": tokens * args.steps / elapsed, "unit": "query-tokens/s"})
         achieved = flops / (attn_us * 1e-6) / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+                           "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                           "traffic": stored_traffic(args.workload, call, args.partition)}
         res["prefill_causal_flops_per_step"] = flops
         cfg.update({"prior_tokens": int(case.prior_lens[0]), "chunk_tokens": int(case.q_lens[0]), "causal": True})
     else:
@@ -273,7 +308,8 @@ def main(argv=None) -> int:
         res.update({"value": case.num_seqs * args.steps / elapsed, "unit": "seq-steps/s"})
         achieved = ab_unique / (attn_us * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+                           "frac": achieved / HBM_PEAK_GBPS,
+                           "traffic": stored_traffic(args.workload, call, args.partition)}
         res["kv_gb_per_s"] = {"logical": kv_logical / (attn_us * 1e-6) / 1e9,
                               "unique": kv_unique / (attn_us * 1e-6) / 1e9}
         res["hbm_peak_frac"] = achieved / HBM_PEAK_GBPS

@@ -488,12 +488,23 @@ void decode_kernel(DecodeParams p) {
   }
 }
 
-// Log-sum-exp merge of the split-KV partials: one wave per (query head, sequence).
+// Log-sum-exp merge of the split-KV partials: one workgroup of 256 threads per
+// (query head, sequence). A thread owns 4 consecutive columns (one 16-byte
+// load per partition) of every NPG-th partition, NPG = 256 / (D/4) partition
+// groups run side by side, and the groups are combined through LDS:
+//   M = max_p m_p,  w_p = 2^(m_p - M),  o = sum_p w_p acc_p / sum_p w_p l_p.
+constexpr int kMergeThreads = 256;
+
 template <DT dt, int D>
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(kMergeThreads)
 void splitkv_merge_kernel(DecodeParams p) {
-  constexpr int CPL = D / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  constexpr int TPR = D / 4;                       // threads per partition row
+  constexpr int NPG = kMergeThreads / TPR;         // partition groups
+  __shared__ float s_max[kMergeThreads / 64];
+  __shared__ float s_num[NPG][D];
+  __shared__ float s_den[NPG];
+  const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int col = (t % TPR) * 4, grp = t / TPR;
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   const int np = min((nblk + p.partition_blocks - 1) / p.partition_blocks, p.max_parts);
@@ -502,21 +513,34 @@ void splitkv_merge_kernel(DecodeParams p) {
   const float* pa_ = p.ws_acc + row * p.max_parts * D;
 
   float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * i]);
+  for (int i = t; i < np; i += kMergeThreads) M = fmaxf(M, ml[2 * i]);
   M = wave_max(M);
-  float num[CPL], den = 0.f;
+  if ((t & 63) == 0) s_max[t >> 6] = M;
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) num[k] = 0.f;
-  for (int i = 0; i < np; ++i) {
+  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_max[w]);
+
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 4
+  for (int i = grp; i < np; i += NPG) {
     const float mi = ml[2 * i], li = ml[2 * i + 1];
     const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(pa_ + (int64_t)i * D + col);
     den = fmaf(w, li, den);
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) num[k] = fmaf(w, pa_[(int64_t)i * D + lane + 64 * k], num[k]);
+    for (int k = 0; k < 4; ++k) num[k] = fmaf(w, a[k], num[k]);
   }
 #pragma unroll
-  for (int k = 0; k < CPL; ++k)
-    store_elem<dt>(p.out, row * D + lane + 64 * k, den > 0.f ? num[k] / den : 0.f);
+  for (int k = 0; k < 4; ++k) s_num[grp][col + k] = num[k];
+  if (t % TPR == 0) s_den[grp] = den;
+  __syncthreads();
+  for (int d = t; d < D; d += kMergeThreads) {
+    float n = 0.f, dn = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < NPG; ++g2) { n += s_num[g2][d]; dn += s_den[g2]; }
+    store_elem<dt>(p.out, row * D + d, dn > 0.f ? n / dn : 0.f);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -544,7 +568,7 @@ static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D>), dim3(p.num_q_heads, p.num_seqs), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D>), dim3(p.num_q_heads, p.num_seqs), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 
