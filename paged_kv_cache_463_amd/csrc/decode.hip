@@ -240,7 +240,7 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
   return s_pick;
 }
 
-template <DT dt, int D, int G, int W, bool SPLIT>
+template <DT dt, int D, int G, int W, bool SPLIT, int NB>
 __global__ __launch_bounds__(64 * W)
 void decode_kernel(DecodeParams p) {
   constexpr int E = Elem<dt>::bytes;
@@ -295,7 +295,10 @@ void decode_kernel(DecodeParams p) {
     off[j] = (uint32_t)((((r + ROWS * j) * p.num_kv_heads + g) * D) * E + c * 16);
 
   const float sl2 = p.scale * kLog2e;
-  const int32_t* tbl = p.block_tables + (int64_t)b * p.block_table_stride;
+  // constant address space: the uniform table lookups stay scalar loads even
+  // where an asm statement below tells the compiler that memory may change
+  const __attribute__((address_space(4))) int32_t* tbl =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.block_table_stride);
   const char* kc = static_cast<const char*>(p.k_cache);
   const char* vc = static_cast<const char*>(p.v_cache);
 
@@ -336,13 +339,33 @@ void decode_kernel(DecodeParams p) {
       reduce_scatter<G, LPR>(v);
       x[j] = v[0] * sl2;
     }
+    // Dead rows (past the end, or the whole block when its id is out of
+    // range) may hold stale NaN: their scores become -inf and their V slices
+    // never reach an accumulator. fp32 zeroes the slices; the 16-bit types
+    // instead switch the byte selectors that split V into token pairs to the
+    // constant-zero selector, which leaves the loaded registers untouched (no
+    // copies, no early wait on the V loads).
     const int tok0 = i * kBlockSize;
+    uint32_t sel_lo[TPL / 2 > 0 ? TPL / 2 : 1], sel_hi[TPL / 2 > 0 ? TPL / 2 : 1];
+#pragma unroll
+    for (int j = 0; j < TPL / 2; ++j) {
+      sel_lo[j] = 0x05040100u;                // column 2i of tokens (j, j+1)
+      sel_hi[j] = 0x07060302u;                // column 2i+1
+    }
     if (!ok || tok0 + kBlockSize > L) {      // uniform: only a sequence's last block
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         if (!ok || tok0 + r + ROWS * j >= L) {
           x[j] = -INFINITY;
-          vb[j] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (dt == DT::F32) {
+            vb[j] = u32x4{0u, 0u, 0u, 0u};
+          } else if ((j & 1) == 0) {         // byte selector 12 yields 0x00
+            sel_lo[j / 2] = (sel_lo[j / 2] & 0xFFFF0000u) | 0x0C0Cu;
+            sel_hi[j / 2] = (sel_hi[j / 2] & 0xFFFF0000u) | 0x0C0Cu;
+          } else {
+            sel_lo[j / 2] = (sel_lo[j / 2] & 0xFFFFu) | 0x0C0C0000u;
+            sel_hi[j / 2] = (sel_hi[j / 2] & 0xFFFFu) | 0x0C0C0000u;
+          }
         }
       }
     }
@@ -398,8 +421,8 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t v0 = vb[j][i], v1 = vb[j + 1][i];
-          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);   // column 2i of both tokens
-          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);   // column 2i+1
+          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, sel_lo[j / 2]);   // column 2i of both tokens
+          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, sel_hi[j / 2]);   // column 2i+1
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const uint32_t ph = __float_as_uint(pg[h]);
@@ -411,25 +434,48 @@ void decode_kernel(DecodeParams p) {
     }
   };
 
-  // blocks first, first + STEP, ... ; two register buffers
-  u32x4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
+  // blocks first, first + STEP, ... through NB register buffers: all NB are in
+  // flight before the first block is computed, and each buffer is refilled
+  // with the block NB steps ahead as soon as it has been consumed. The loop
+  // runs whole rounds of NB blocks and is left only at the end of a round
+  // (the fewer than NB blocks left over are computed after it), so every path
+  // back to the loop head has issued the refills in the same order as the
+  // prologue and the compiler's load counters wait only for the buffer about
+  // to be used.
+  u32x4 kbuf[NB][TPL], vbuf[NB][TPL];
+  bool okb[NB];
   const int first = SPLIT ? lo : lo + wave;
   if (first < hi) {
-    // both buffers in flight before the first block is computed; each buffer is
-    // refilled with the block two steps ahead as soon as it has been consumed
-    bool okA = fetch(block_id(first), kA, vA);
-    bool okB = fetch(block_id(first + STEP), kB, vB);
-    int bid = block_id(first + 2 * STEP);
-    for (int i = first;; i += 2 * STEP) {
-      process(i, kA, vA, okA);
-      okA = fetch(bid, kA, vA);
-      bid = block_id(i + 3 * STEP);
-      if (i + STEP >= hi) break;
-      process(i + STEP, kB, vB, okB);
-      okB = fetch(bid, kB, vB);
-      bid = block_id(i + 4 * STEP);
-      if (i + 2 * STEP >= hi) break;
+    // buffers issued in order (an empty asm that clobbers memory keeps the
+    // loads of buffer k+1 behind those of buffer k), as inside the loop
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      okb[k] = fetch(block_id(first + k * STEP), kbuf[k], vbuf[k]);
+      asm volatile("" ::: "memory");
     }
+    int bid = block_id(first + NB * STEP);
+    int i = first;
+    for (; i + (NB - 1) * STEP < hi; i += NB * STEP) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        process(i + k * STEP, kbuf[k], vbuf[k], okb[k]);
+        // The refill must follow the last use of the buffer it overwrites:
+        // were it hoisted, the register allocator would give the buffer two
+        // homes, and the copies at the loop latch wait for every load in
+        // flight. The accumulators pass through an empty asm that clobbers
+        // memory, so the P.V that produces them completes before it and no
+        // load moves above it.
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) asm volatile("" : "+v"(acc[h][e])::"memory");
+        okb[k] = fetch(bid, kbuf[k], vbuf[k]);
+        bid = block_id(i + (k + NB + 1) * STEP);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k + 1 < NB; ++k)
+      if (i + k * STEP < hi) process(i + k * STEP, kbuf[k], vbuf[k], okb[k]);
   }
 
   // sum the ROWS row-streams of the wave (lanes of one c share the head order)
@@ -546,6 +592,18 @@ void splitkv_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+// Register buffers of K/V blocks in flight per wave (bytes in flight per CU
+// bound the bandwidth: the large-group kernels run fewer waves per SIMD).
+#ifndef PA_DECODE_NB_SMALLG
+#define PA_DECODE_NB_SMALLG 2
+#endif
+#ifndef PA_DECODE_NB_LARGEG
+#define PA_DECODE_NB_LARGEG 2
+#endif
+constexpr int decode_buffers(DT dt, int D, int G) {
+  return (dt == DT::F32 && D == 128) ? 2 : (G >= 4 ? PA_DECODE_NB_LARGEG : PA_DECODE_NB_SMALLG);
+}
+
 // Waves per workgroup; fp32 with head_dim 128 holds twice the bytes per lane
 // and stays at 4 waves so that its registers fit without spilling.
 template <DT dt, int D, bool SPLIT>
@@ -560,10 +618,10 @@ static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_kv_heads, p.num_seqs, SPLIT ? (p.max_parts + W - 1) / W : 1);
   dim3 block(64 * W);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<dt, D, 2, W, SPLIT>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<dt, D, 4, W, SPLIT>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<dt, D, 8, W, SPLIT>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT, decode_buffers(dt, D, 1)>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<dt, D, 2, W, SPLIT, decode_buffers(dt, D, 2)>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<dt, D, 4, W, SPLIT, decode_buffers(dt, D, 4)>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<dt, D, 8, W, SPLIT, decode_buffers(dt, D, 8)>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
