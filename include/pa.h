@@ -133,7 +133,7 @@ PA_API int32_t pa_decode(void* out, const void* query, const void* k_cache, cons
 /*
  * Bytes of device workspace pa_decode_splitkv needs: per (sequence, query
  * head, partition) one fp32 partial output row of head_dim plus its running
- * max and normaliser. Returns 0 for non-positive sizes.
+ * max and normaliser, and one work counter. Returns 0 for non-positive sizes.
  */
 PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);
@@ -151,7 +151,9 @@ PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_
  *   partition_size   tokens per partition, a positive multiple of 16
  *   workspace        device buffer of at least
  *                    pa_decode_splitkv_workspace_bytes(...) bytes, 16-byte
- *                    aligned; contents on entry are ignored
+ *                    aligned; contents on entry are ignored. Calls that
+ *                    share a workspace must not overlap (same stream, or
+ *                    ordered by the caller)
  */
 PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, const void* v_cache,
                           int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,

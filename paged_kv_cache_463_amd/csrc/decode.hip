@@ -38,11 +38,11 @@
 //   * Block ids are wave-uniform (scalar loads, read a step ahead); two register
 //     buffers keep the next block's K/V loads in flight while a block is computed.
 //
-// Split-KV: wave w of workgroup (kv head, sequence, z) covers partition
-// p = W*z + w, logical tokens [partition_size*p, partition_size*(p+1)), on its
-// own and writes, per query head, the unnormalised output row plus (max,
-// normaliser) to the workspace; a second kernel merges partitions by
-// log-sum-exp.
+// Split-KV: every wave covers one (kv head, sequence, partition p) item,
+// logical tokens [partition_size*p, partition_size*(p+1)), on its own, and
+// writes, per query head, the unnormalised output row plus (max, normaliser)
+// to the workspace; a second kernel merges partitions by log-sum-exp. Items
+// are handed out by a work counter (see split_work).
 #include <math.h>
 
 #include "pa_device.h"
@@ -240,6 +240,81 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
   return s_pick;
 }
 
+// Split-KV work assignment. A work item is one (kv head, sequence, partition)
+// triple that exists. Workgroups start in grid order, and the compute units
+// of the chip do not all finish their share at the same rate (each XCD takes
+// every eighth workgroup, and some XCDs run slower than others), so items are
+// not bound to grid positions: thread 0 of each workgroup takes W consecutive
+// tickets from a work counter (zeroed before the launch) and wave w takes
+// ticket t + w. Tickets run over the kv heads fastest, then over the
+// (sequence, partition) pairs numbered densely, sequence by sequence and the
+// partitions of a sequence in order; the grid carries a quarter more
+// workgroups than the largest possible number of items needs, so a slow part
+// of the chip simply takes fewer tickets and the spare workgroups find none.
+// Every workgroup computes the per-sequence prefix sums of partition counts
+// in LDS. Batches above kRankMaxSeqs sequences number all num_seqs *
+// max_parts pairs instead, empty ones included.
+template <int NT>
+__device__ __forceinline__ bool split_work(const DecodeParams& p, int wave, int& g, int& b, int& part) {
+  __shared__ int s_pre[kRankMaxSeqs + 1];
+  __shared__ int s_ticket;
+  const int B = p.num_seqs;
+  const bool dense = B <= kRankMaxSeqs;
+  if (threadIdx.x == 0) s_ticket = atomicAdd(p.ws_ctr, NT / 64);
+  if (dense) {
+    for (int t = threadIdx.x; t < B; t += NT) {
+      const int L = max(p.context_lens[t], 0);
+      const int nb = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
+      s_pre[t] = (nb + p.partition_blocks - 1) / p.partition_blocks;
+    }
+  }
+  __syncthreads();
+  if (dense && threadIdx.x < 64) {          // exclusive scan, a run of sequences per lane
+    const int l = threadIdx.x;
+    const int per = (B + 63) / 64;
+    const int t0 = min(l * per, B), t1 = min(t0 + per, B);
+    int run = 0;
+    for (int t = t0; t < t1; ++t) run += s_pre[t];
+    int inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (l >= o) inc += y;
+    }
+    int acc = inc - run;
+    for (int t = t0; t < t1; ++t) {
+      const int c = s_pre[t];
+      s_pre[t] = acc;
+      acc += c;
+    }
+    if (l == 63) s_pre[B] = inc;
+  }
+  __syncthreads();
+  // LDS reads at uniform addresses, made visibly uniform so that the search,
+  // the exit and everything derived from (g, b, part) stay scalar
+  const int ticket = __builtin_amdgcn_readfirstlane(s_ticket) + wave;
+  g = ticket % p.num_kv_heads;
+  const int item = ticket / p.num_kv_heads;
+  if (!dense) {
+    b = item / p.max_parts;
+    part = item % p.max_parts;
+    return b < B;
+  }
+  if (item >= __builtin_amdgcn_readfirstlane(s_pre[B])) return false;
+  int lo = 0, hi = B - 1;                   // last sequence whose first item is <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= item) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  part = item - __builtin_amdgcn_readfirstlane(s_pre[lo]);
+  return true;
+}
+
+__global__ void splitkv_reset_kernel(int32_t* ctr) {
+  if (threadIdx.x == 0) *ctr = 0;
+}
+
 template <DT dt, int D, int G, int W, bool SPLIT, int NB>
 __global__ __launch_bounds__(64 * W)
 void decode_kernel(DecodeParams p) {
@@ -263,20 +338,24 @@ void decode_kernel(DecodeParams p) {
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int own = HM::owner(c);
-  const int g = blockIdx.x;
-  const int b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
-  const int part = SPLIT ? (int)blockIdx.z * W + wave : 0;
+  int g, b, part = 0;
+  if constexpr (SPLIT) {
+    if (!split_work<64 * W>(p, wave, g, b, part)) return;   // no work item left
+  } else {
+    g = blockIdx.x;
+    b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
+  }
   const int hq0 = g * G;
 
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   // single pass: the W waves share the sequence's blocks round-robin.
-  // split-KV: wave w walks partition W*z + w on its own (no merge across waves)
+  // split-KV: every wave walks one partition on its own (no merge across waves)
   constexpr int STEP = SPLIT ? 1 : W;
   int lo = 0, hi = nblk;
   if constexpr (SPLIT) {
     lo = part * p.partition_blocks;
-    if (lo >= nblk) return;                 // this wave's partition lies past the end
+    if (lo >= nblk) return;                 // only where empty pairs are numbered too
     hi = min(nblk, lo + p.partition_blocks);
   }
 
@@ -615,7 +694,14 @@ template <DT dt, int D, bool SPLIT>
 static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   constexpr int W = decode_waves<dt, D, SPLIT>();
   const int G = p.num_q_heads / p.num_kv_heads;
-  dim3 grid(p.num_kv_heads, p.num_seqs, SPLIT ? (p.max_parts + W - 1) / W : 1);
+  dim3 grid(p.num_kv_heads, p.num_seqs, 1);
+  if constexpr (SPLIT) {                   // work items are handed out by a counter
+    hipLaunchKernelGGL(splitkv_reset_kernel, dim3(1), dim3(64), 0, s, p.ws_ctr);
+    const int64_t items = (int64_t)p.num_kv_heads * p.num_seqs * p.max_parts;
+    const int64_t wgs = (items + items / 4 + W - 1) / W;
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    grid = dim3((unsigned)wgs);
+  }
   dim3 block(64 * W);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT, decode_buffers(dt, D, 1)>), grid, block, 0, s, p); break;
