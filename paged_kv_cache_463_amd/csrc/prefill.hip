@@ -215,18 +215,23 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
   };
-  // issue the loads of K tile tk (table entry kbid) into sK[kb] and V tile tv
-  // (entry vbid) into sV[vb]; tiles past the end re-read the last tile, so
-  // every wave issues the same loads
+  // the loads of K tile tk (table entry kbid) into sK[kb] and V tile tv
+  // (entry vbid) into sV[vb]: 2*NI instructions, issued one at a time by
+  // dma_part (a burst of them stalls the wave behind the address unit); tiles
+  // past the end re-read the last tile, so every wave issues the same loads
+  struct DmaJob { const char* ks; const char* vs; const uint8_t* kd; const uint8_t* vd; };
+  auto dma_job = [&](int tk, int kbid, int kb, int tv, int vbid, int vb) -> DmaJob {
+    return {kc + block_base(tk, kbid), vc + block_base(tv, vbid), &sK[kb][wave * kBlockSize * RB],
+            &sV[vb][wave * kBlockSize * RB]};
+  };
+  auto dma_part = [&](const DmaJob& j, int n) {      // n in [0, 2*NI)
+    if (n < NI) lds_load16(j.ks, k_src[n], j.kd + n * 1024);
+    else lds_load16(j.vs, v_src[n - NI], j.vd + (n - NI) * 1024);
+  };
   auto dma = [&](int tk, int kbid, int kb, int tv, int vbid, int vb) {
-    const char* ks = kc + block_base(tk, kbid);
-    const char* vs = vc + block_base(tv, vbid);
-    const uint8_t* kd = &sK[kb][wave * kBlockSize * RB];
-    const uint8_t* vd = &sV[vb][wave * kBlockSize * RB];
+    const DmaJob j = dma_job(tk, kbid, kb, tv, vbid, vb);
 #pragma unroll
-    for (int n = 0; n < NI; ++n) lds_load16(ks, k_src[n], kd + n * 1024);
-#pragma unroll
-    for (int n = 0; n < NI; ++n) lds_load16(vs, v_src[n], vd + n * 1024);
+    for (int n = 0; n < 2 * NI; ++n) dma_part(j, n);
   };
   // wait for this wave's loads; in the last V tile zero the rows of keys past
   // kend (stale slots) in this wave's block, then make everything visible
@@ -281,7 +286,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
 
   for (int t = 0; t < nkt; ++t) {
     const int key0 = t * kBK;
-    dma(t + 2, kbid_next, t & 1, t + 1, vbid_next, (t + 1) & 1);
+    const DmaJob job = dma_job(t + 2, kbid_next, t & 1, t + 1, vbid_next, (t + 1) & 1);
 
     // scale; mask (uniform: only tiles that reach the causal diagonal or the
     // end of the keys); tile max of the column; rare rescale
@@ -314,15 +319,26 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     }
     const float mu = (mref == -INFINITY) ? 0.f : mref;
 
-    // scores of tile t+1 (matrix cores) interleaved with P of tile t (VALU):
     // P = 2^(s - m) rounded to the input type, normaliser from the rounded
-    // values. Step ds issues the two MFMAs of k-step ds and the exp / pack /
-    // sum of PPS pairs of scores; a scheduling barrier closes each step so the
-    // matrix and vector streams stay interleaved. The last iteration computes
-    // scores it never uses (its buffer holds an older tile).
+    // values; pair pr (0..15) of this lane's scores is (kt, ss, e2).
     u32x4 pk[2][2];                           // [kt][16-key step]: packed P pairs
+    auto make_p = [&](int pr) {
+      const int kt = pr >> 3, ss = (pr >> 2) & 1, e2 = pr & 3;
+      const float p0 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2], sl2, -mu));
+      const float p1 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2 + 1], sl2, -mu));
+      pk[kt][ss][e2] = M::pack(p0, p1);
+      lsum = M::sum2(pk[kt][ss][e2], lsum);
+    };
+    // Scores of tile t+1 (matrix cores) interleaved with the P of keys 0..31
+    // of tile t (VALU); the P of keys 32..63 is made during the first half of
+    // the P.V products below, which only use keys 0..31, so both phases carry
+    // vector work for the matrix cores to overlap. Step ds issues the two
+    // MFMAs of k-step ds and its share of the pairs; a scheduling barrier
+    // closes each step so the matrix and vector streams stay interleaved. The
+    // last iteration computes scores it never uses (its buffer holds an older
+    // tile).
     {
-      constexpr int PPS = 16 / DS;            // score pairs per k-step
+      constexpr int PPS = 8 / DS;             // pairs of keys 0..31 per k-step
       const uint8_t* Kn = sK[(t + 1) & 1];
       auto kfrag = [&](int kt, int ds) {
         const int r = kt * 32 + col;
@@ -337,6 +353,9 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
           ka[(ds + 1) & 1][0] = kfrag(0, ds + 1);
           ka[(ds + 1) & 1][1] = kfrag(1, ds + 1);
         }
+        // this tile's global -> LDS loads, spread over the k-steps
+#pragma unroll
+        for (int n = ds * 2 * NI / DS; n < (ds + 1) * 2 * NI / DS; ++n) dma_part(job, n);
         if (ds == 0) {
           const f32x16 z = {};
           sn[0] = M::run(ka[0][0], qreg[0], z);
@@ -346,22 +365,10 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
           sn[1] = M::run(ka[ds & 1][1], qreg[ds], sn[1]);
         }
 #pragma unroll
-        for (int j = 0; j < PPS; ++j) {
-          const int pr = ds * PPS + j;        // pair index 0..15: (kt, ss, e2)
-          const int kt = pr >> 3, ss = (pr >> 2) & 1, e2 = pr & 3;
-          const float p0 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2], sl2, -mu));
-          const float p1 = fast_exp2(fmaf(sc[kt][8 * ss + 2 * e2 + 1], sl2, -mu));
-          pk[kt][ss][e2] = M::pack(p0, p1);
-          lsum = M::sum2(pk[kt][ss][e2], lsum);
-        }
+        for (int j = 0; j < PPS; ++j) make_p(ds * PPS + j);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    vec pb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) pb[kt][ss] = as_vec<vec>(pk[kt][ss]);
 
     // O^T += V^T P^T over V(t). The A operand (32 head-dim rows x 16 keys) is
     // read from row-major V with two transposing 8-byte reads: in each group of
@@ -389,6 +396,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
       // step i: key step ks = i / MD of the 64 keys, output tile md = i % MD, so
       // consecutive MFMAs accumulate into different tiles
       constexpr int NV = MD * 4;
+      constexpr int PPV = 8 / (NV / 2);       // pairs of keys 32..63 per step of the first half
       auto vstep = [&](int i) { return vfrag(i % MD, (i / MD) >> 1, (i / MD) & 1); };
       vec va[3];
       va[0] = vstep(0);
@@ -397,7 +405,13 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
       for (int i = 0; i < NV; ++i) {
         if (i + 2 < NV) va[(i + 2) % 3] = vstep(i + 2);
         const int md = i % MD, ks = i / MD;
-        o[md] = M::run(va[i % 3], pb[ks >> 1][ks & 1], o[md]);
+        if (i < NV / 2) {
+#pragma unroll
+          for (int j = 0; j < PPV; ++j) make_p(8 + i * PPV + j);
+        }
+        const vec pbk = as_vec<vec>(pk[ks >> 1][ks & 1]);
+        o[md] = M::run(va[i % 3], pbk, o[md]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
