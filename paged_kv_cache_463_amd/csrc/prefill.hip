@@ -263,7 +263,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   // then accumulates P V of tile t. K runs one tile ahead of V in LDS: during
   // iteration t the wave reads K(t+1) and V(t) and the workgroup writes K(t+2)
   // and V(t+1) into the other two buffers; one barrier per tile.
-  f32x16 sc[2], sn[2];                       // scores of the current / next tile
+  f32x16 sa[2], sb[2];                       // scores of two consecutive tiles
   dma(0, entry(0), 0, 0, entry(0), 0);
   land(0, 0);
   dma(1, entry(1), 1, nkt, entry(nkt), 1);    // K(1); the V part re-reads tile nkt-1 into sV[1]
@@ -274,17 +274,20 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const f32x16 z = {};
-      sc[kt] = z;
+      sa[kt] = z;
       const int r = kt * 32 + col;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
-        sc[kt] = M::run(as_vec<vec>(*reinterpret_cast<const u32x4*>(&K0[r * RB + (((2 * ds + hi) ^ kswz(r)) << 4)])),
-                        qreg[ds], sc[kt]);
+        sa[kt] = M::run(as_vec<vec>(*reinterpret_cast<const u32x4*>(&K0[r * RB + (((2 * ds + hi) ^ kswz(r)) << 4)])),
+                        qreg[ds], sa[kt]);
     }
   }
   land(nkt, 1);
 
-  for (int t = 0; t < nkt; ++t) {
+  // one tile; sc holds the scores of tile t, sn receives those of tile t+1.
+  // The loop below runs two tiles per trip with the two score arrays trading
+  // roles, so no copy from sn to sc is needed.
+  auto key_tile = [&](const int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int key0 = t * kBK;
     const DmaJob job = dma_job(t + 2, kbid_next, t & 1, t + 1, vbid_next, (t + 1) & 1);
 
@@ -417,9 +420,13 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
     vbid_next = entry(t + 2);                 // loads complete during the wait below
     land(t + 1, (t + 1) & 1);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) sc[kt] = sn[kt];
+  };
+  int t = 0;
+  for (; t + 1 < nkt; t += 2) {
+    key_tile(t, sa, sb);
+    key_tile(t + 1, sb, sa);
   }
+  if (t < nkt) key_tile(t, sa, sb);
 
   // ---- normalise and store ------------------------------------------------
   const float l = lsum + __shfl_xor(lsum, 32);
