@@ -304,11 +304,19 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
           sc[kt][r] = vis ? sc[kt][r] : -INFINITY;
         }
     }
-    float tmax = -INFINITY;                   // on raw scores (scale > 0)
+    // tile max of the column (raw scores, scale > 0) by a balanced tree of
+    // 3-input maxima; rare rescale
+    float tmax;
+    {
+      auto v = [&](int j) { return sc[j >> 4][j & 15]; };
+      auto mx3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+      float l1[11];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(sc[kt][r], sc[kt][r + 1]));
+      for (int i = 0; i < 10; ++i) l1[i] = mx3(v(3 * i), v(3 * i + 1), v(3 * i + 2));
+      l1[10] = fmaxf(v(30), v(31));
+      tmax = fmaxf(mx3(mx3(l1[0], l1[1], l1[2]), mx3(l1[3], l1[4], l1[5]), mx3(l1[6], l1[7], l1[8])),
+                   fmaxf(l1[9], l1[10]));
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;
     if (__any(tmax > mref + kSlack)) {
       const float mn = fmaxf(mref, tmax);
