@@ -133,8 +133,7 @@ PA_API int32_t pa_decode(void* out, const void* query, const void* k_cache, cons
 /*
  * Bytes of device workspace pa_decode_splitkv needs: per (sequence, query
  * head, partition) one fp32 partial output row of head_dim plus its running
- * max and normaliser, plus a work counter and a table of the (sequence,
- * partition) pairs. Returns 0 for non-positive sizes.
+ * max and normaliser, and one work counter. Returns 0 for non-positive sizes.
  */
 PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);

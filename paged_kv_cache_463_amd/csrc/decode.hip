@@ -245,69 +245,74 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
 // of the chip do not all finish their share at the same rate (each XCD takes
 // every eighth workgroup, and some XCDs run slower than others), so items are
 // not bound to grid positions: thread 0 of each workgroup takes W consecutive
-// tickets from a work counter and wave w takes ticket t + w. Tickets run over
-// the kv heads fastest, then over the (sequence, partition) pairs that exist,
-// numbered densely, sequence by sequence and the partitions of a sequence in
-// order; a table of those pairs, their count and the zeroed counter are
-// written once per call by splitkv_prep_kernel. The grid carries a quarter
-// more workgroups than the largest possible number of items needs, so a slow
-// part of the chip simply takes fewer tickets and the spare workgroups find
-// none.
-constexpr int kPrepThreads = 1024;
-
-__global__ __launch_bounds__(kPrepThreads) void splitkv_prep_kernel(DecodeParams p) {
-  __shared__ int s_wave[kPrepThreads / 64];
-  __shared__ int s_base;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) s_base = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < p.num_seqs; c0 += kPrepThreads) {
-    const int t = c0 + tid;
-    int n = 0;                                // partitions of sequence t
-    if (t < p.num_seqs) {
+// tickets from a work counter (zeroed before the launch) and wave w takes
+// ticket t + w. Tickets run over the kv heads fastest, then over the
+// (sequence, partition) pairs numbered densely, sequence by sequence and the
+// partitions of a sequence in order; the grid carries a quarter more
+// workgroups than the largest possible number of items needs, so a slow part
+// of the chip simply takes fewer tickets and the spare workgroups find none.
+// Every workgroup computes the per-sequence prefix sums of partition counts
+// in LDS. Batches above kRankMaxSeqs sequences number all num_seqs *
+// max_parts pairs instead, empty ones included.
+template <int NT>
+__device__ __forceinline__ bool split_work(const DecodeParams& p, int wave, int& g, int& b, int& part) {
+  __shared__ int s_pre[kRankMaxSeqs + 1];
+  __shared__ int s_ticket;
+  const int B = p.num_seqs;
+  const bool dense = B <= kRankMaxSeqs;
+  if (threadIdx.x == 0) s_ticket = atomicAdd(p.ws_ctr, NT / 64);
+  if (dense) {
+    for (int t = threadIdx.x; t < B; t += NT) {
       const int L = max(p.context_lens[t], 0);
       const int nb = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-      n = (nb + p.partition_blocks - 1) / p.partition_blocks;
+      s_pre[t] = (nb + p.partition_blocks - 1) / p.partition_blocks;
     }
-    int inc = n;                              // inclusive scan: wave, then across waves
+  }
+  __syncthreads();
+  if (dense && threadIdx.x < 64) {          // exclusive scan, a run of sequences per lane
+    const int l = threadIdx.x;
+    const int per = (B + 63) / 64;
+    const int t0 = min(l * per, B), t1 = min(t0 + per, B);
+    int run = 0;
+    for (int t = t0; t < t1; ++t) run += s_pre[t];
+    int inc = run;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
+      if (l >= o) inc += y;
     }
-    if (lane == 63) s_wave[wv] = inc;
-    __syncthreads();
-    int before = s_base;
-    for (int w = 0; w < wv; ++w) before += s_wave[w];
-    const int first = before + inc - n;
-    for (int k = 0; k < n; ++k) p.ws_items[first + k] = make_int2(t, k);
-    __syncthreads();
-    if (tid == kPrepThreads - 1) s_base = first + n;
-    __syncthreads();
+    int acc = inc - run;
+    for (int t = t0; t < t1; ++t) {
+      const int c = s_pre[t];
+      s_pre[t] = acc;
+      acc += c;
+    }
+    if (l == 63) s_pre[B] = inc;
   }
-  if (tid == 0) {
-    p.ws_ctl[0] = 0;                          // ticket counter
-    p.ws_ctl[1] = s_base;                     // number of (sequence, partition) pairs
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ bool split_work(const DecodeParams& p, int wave, int& g, int& b, int& part) {
-  __shared__ int s_ticket;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&p.ws_ctl[0], NT / 64);
   __syncthreads();
-  // the table and the count were written by the previous kernel and stay
-  // constant here: read them through the constant address space (scalar loads)
-  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
-  typedef const __attribute__((address_space(4))) int2* cint2_ptr;
+  // LDS reads at uniform addresses, made visibly uniform so that the search,
+  // the exit and everything derived from (g, b, part) stay scalar
   const int ticket = __builtin_amdgcn_readfirstlane(s_ticket) + wave;
   g = ticket % p.num_kv_heads;
   const int item = ticket / p.num_kv_heads;
-  if (item >= ((cint_ptr)p.ws_ctl)[1]) return false;
-  const int2 bp = ((cint2_ptr)p.ws_items)[item];
-  b = bp.x;
-  part = bp.y;
+  if (!dense) {
+    b = item / p.max_parts;
+    part = item % p.max_parts;
+    return b < B;
+  }
+  if (item >= __builtin_amdgcn_readfirstlane(s_pre[B])) return false;
+  int lo = 0, hi = B - 1;                   // last sequence whose first item is <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= item) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  part = item - __builtin_amdgcn_readfirstlane(s_pre[lo]);
   return true;
+}
+
+__global__ void splitkv_reset_kernel(int32_t* ctr) {
+  if (threadIdx.x == 0) *ctr = 0;
 }
 
 template <DT dt, int D, int G, int W, bool SPLIT, int NB>
@@ -350,7 +355,7 @@ void decode_kernel(DecodeParams p) {
   int lo = 0, hi = nblk;
   if constexpr (SPLIT) {
     lo = part * p.partition_blocks;
-    if (lo >= nblk) return;                 // not for a listed pair (kept as a guard)
+    if (lo >= nblk) return;                 // only where empty pairs are numbered too
     hi = min(nblk, lo + p.partition_blocks);
   }
 
@@ -691,7 +696,7 @@ static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const int G = p.num_q_heads / p.num_kv_heads;
   dim3 grid(p.num_kv_heads, p.num_seqs, 1);
   if constexpr (SPLIT) {                   // work items are handed out by a counter
-    hipLaunchKernelGGL(splitkv_prep_kernel, dim3(1), dim3(kPrepThreads), 0, s, p);
+    hipLaunchKernelGGL(splitkv_reset_kernel, dim3(1), dim3(64), 0, s, p.ws_ctr);
     const int64_t items = (int64_t)p.num_kv_heads * p.num_seqs * p.max_parts;
     const int64_t wgs = (items + items / 4 + W - 1) / W;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;

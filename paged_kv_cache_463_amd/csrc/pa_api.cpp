@@ -154,13 +154,11 @@ size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
     return 0;
   const int64_t parts = ceil_div(max_context_len, partition_size);
   const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
-  // fp32 partial outputs, then (max, normaliser) pairs, then the work counter
-  // and pair count, then the table of (sequence, partition) pairs; each part
-  // 256-byte aligned
+  // fp32 partial outputs, then (max, normaliser) pairs, then the work counter;
+  // each part 256-byte aligned
   const int64_t acc_bytes = ceil_div(rows * head_dim * 4, 256) * 256;
   const int64_t ml_bytes = ceil_div(rows * 2 * 4, 256) * 256;
-  const int64_t item_bytes = ceil_div((int64_t)num_seqs * parts * 8, 256) * 256;
-  return (size_t)(acc_bytes + ml_bytes + 256 + item_bytes);
+  return (size_t)(acc_bytes + ml_bytes + 256);
 }
 
 int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -192,9 +190,8 @@ int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, con
   p.ws_acc = static_cast<float*>(workspace);
   const int64_t acc_bytes = ceil_div(rows * head_dim * 4, 256) * 256;
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes);
-  char* ctl = static_cast<char*>(workspace) + acc_bytes + ceil_div(rows * 2 * 4, 256) * 256;
-  p.ws_ctl = reinterpret_cast<int32_t*>(ctl);
-  p.ws_items = reinterpret_cast<int2*>(ctl + 256);
+  p.ws_ctr = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + acc_bytes +
+                                        ceil_div(rows * 2 * 4, 256) * 256);
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 

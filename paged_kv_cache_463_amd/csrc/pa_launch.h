@@ -42,8 +42,7 @@ struct DecodeParams {
   int32_t max_parts;            // ceil(max_context_len / partition_size)
   float* ws_acc;                // [num_seqs][num_q_heads][max_parts][head_dim]
   float* ws_ml;                 // [num_seqs][num_q_heads][max_parts][2]  (max, normaliser)
-  int32_t* ws_ctl;              // [0] ticket counter, [1] number of listed pairs (set per call)
-  int2* ws_items;               // (sequence, partition) pairs, densely numbered (set per call)
+  int32_t* ws_ctr;              // work counter of the partition kernel (zeroed per call)
 };
 
 struct PrefillParams {
