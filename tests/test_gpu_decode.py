@@ -55,11 +55,14 @@ def test_zero_length_rows_are_zero():
     assert_close(out, ref, "bf16", "zero-length row")
 
 
-@pytest.mark.parametrize("lens", [[17] * 300, [5, 300, 16, 300] * 75, list(range(1, 601)), [0, 3, 0, 1] * 40],
-                         ids=["equal-lengths", "tied-pairs", "600-distinct", "zeros-and-ones"])
+@pytest.mark.parametrize("lens", [[17] * 300, [5, 300, 16, 300] * 75, list(range(1, 601)), [0, 3, 0, 1] * 40,
+                                  [(7 * i) % 61 + 1 for i in range(1100)]],
+                         ids=["equal-lengths", "tied-pairs", "600-distinct", "zeros-and-ones",
+                              "1100-grid-order"])
 def test_many_sequences_each_written_once(lens):
     """Grid rows take sequences longest first through a bucketed ranking on the device; every
-    sequence must be computed exactly once (the output starts NaN-filled)."""
+    sequence must be computed exactly once (the output starts NaN-filled). Batches above 1024
+    sequences keep grid order."""
     case = W.make_decode("order", "bf16", lens, 8, 2, 64, seed=31)
     _run_and_check(case)
 

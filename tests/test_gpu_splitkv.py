@@ -25,6 +25,20 @@ def test_splitkv_shapes(dtype, G, D, part):
     assert_close(out_f64(out), oracle_decode(case, kp, vp), dtype, f"splitkv part={part}")
 
 
+def test_splitkv_batch_above_dense_numbering_limit():
+    """Above 1024 sequences the work items number every (sequence, partition) pair, empty ones
+    included; every output row must still be written once and right (the output starts NaN)."""
+    lens = [(13 * i) % 97 + 1 for i in range(1100)]
+    case = W.make_decode("splitbig", "bf16", lens, 4, 2, 64, seed=41)
+    say(f"case: splitkv B={case.num_seqs} part=32")
+    d = DeviceDecode(case)
+    d.scatter()
+    out = d.decode(split=32)
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    assert_close(out_f64(out), oracle_decode(case, kp, vp), "bf16", "splitkv B=1100")
+
+
 def test_single_partition_agrees_with_single_pass():
     """A partition covering the whole sequence is the same softmax as the single pass. The split
     pass sums a partition in one wave while the single pass merges four waves, so the two agree
