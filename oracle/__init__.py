@@ -24,6 +24,12 @@ the pages it cites:
   page "vLLM推理引擎深度实战" §5.3; the reading is: query i of a chunk sits at
   absolute position ``L - q_len + i`` and sees keys ``0 .. that position``).
 
+``block_manager`` (imported as a module) holds the block manager and the block
+copy / swap definitions: share counts, head-of-free-list allocation, fill then
+new block on append, copy-on-write of a shared block before a write (pages
+"vLLM推理引擎深度解析" §三, "vLLM 原理与源码阅读" Block 管理器, "vLLM推理引擎深度实战"
+§5.3); its pins are in ``tests/test_block_manager_oracle.py``.
+
 Parity pins: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` against something other than itself (torch's
 fp64 ``scaled_dot_product_attention``, 40-digit ``decimal`` brute force, closed
@@ -31,6 +37,7 @@ forms, invariants, golden slot positions derived from the pages' append rule),
 and mutation tests plant mistakes in this oracle to show that the pins catch
 them. No function is "parity unpinned".
 """
+from . import block_manager  # noqa: F401
 from .paged_attention import (  # noqa: F401
     to_f64,
     scatter,
