@@ -73,7 +73,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 4,  /* block_size, head_dim or group size not supported    */
   PA_ERR_WORKSPACE = 5,    /* split-KV workspace missing or too small             */
   PA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch         */
-  PA_ERR_ALIGNMENT = 7     /* a pointer or stride is not 16-byte aligned          */
+  PA_ERR_ALIGNMENT = 7,    /* a pointer or stride is not 16-byte aligned          */
+  PA_ERR_NO_BLOCKS = 8,    /* block manager: not enough free blocks (no change)   */
+  PA_ERR_SEQUENCE = 9      /* block manager: unknown request id, or one in use    */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
@@ -162,6 +164,84 @@ PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cac
                           int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
                           int32_t max_context_len, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * pa_copy_blocks — the device half of copy-on-write ([P2] Block 管理器: requests
+ * that share a prompt prefix share its physical blocks, and a shared block is
+ * copied only when one of them must write into it). For each (src, dst) pair,
+ * the rows of block dst in both pools become those of block src, bit for bit.
+ *
+ *   k_cache, v_cache pools (layout above), written in place
+ *   block_stride     elements between consecutive physical blocks (>= 16*H_kv*D)
+ *   num_blocks       physical blocks in each pool
+ *   num_kv_heads, head_dim, dtype   size of a block's rows: 16*H_kv*D elements
+ *   pairs            int32 [num_pairs][2] (src, dst) in DEVICE memory; pairs
+ *                    with an index outside [0, num_blocks) are skipped
+ * Preconditions: no dst is the src or dst of another pair (the copies run in
+ * parallel). pairs may be NULL only when num_pairs == 0.
+ */
+PA_API int32_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_stride, int64_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype, const int32_t* pairs,
+                              int64_t num_pairs, void* stream);
+
+/*
+ * pa_swap_blocks — move whole blocks between a device pool and a host pool
+ * (the CPU swap space of [P3] §5.3): for each (src, dst) pair, block dst of
+ * the destination pool becomes block src of the source pool. Either pool may
+ * be device memory or pinned host memory (the copy engine moves the bytes;
+ * runs of consecutive pairs are merged into one copy). Call once for K and
+ * once for V.
+ *
+ *   dst_pool, dst_blocks   destination pool and its number of blocks
+ *   src_pool, src_blocks   source pool and its number of blocks
+ *   block_bytes            bytes per block (block_stride * element bytes)
+ *   pairs                  int64 [num_pairs][2] (src, dst) in HOST memory
+ * Every pair is checked on the host before any copy is issued: an index
+ * outside its pool returns PA_ERR_SHAPE and moves nothing. Asynchronous on
+ * `stream`; host memory that is not pinned makes the copies synchronous.
+ */
+PA_API int32_t pa_swap_blocks(void* dst_pool, int64_t dst_blocks, const void* src_pool, int64_t src_blocks,
+                              int64_t block_bytes, const int64_t* pairs, int64_t num_pairs, void* stream);
+
+/*
+ * Host block manager ([P1] §三 PagedAttentionManager, with the copy-on-write of
+ * [P2] Block 管理器). A physical block carries a share count. pa_bm_allocate
+ * gives a new request ceil(num_tokens / block_size) blocks from the head of
+ * the free list, or PA_ERR_NO_BLOCKS and nothing when fewer are free.
+ * pa_bm_append adds one token: it fills the last block, takes a new block
+ * from the head of the free list once that is full, and — when the last block
+ * is shared and not full — takes a fresh block for it, lowers the shared
+ * block's count and returns (cow_src, cow_dst), the pair pa_copy_blocks must
+ * copy before the token's K/V are written (-1, -1 when no copy is needed);
+ * *slot is the new token's slot for pa_reshape_and_cache. pa_bm_share_prefix
+ * lets a new request `child` start with the first num_tokens tokens of `src`
+ * by sharing the ceil(num_tokens / block_size) blocks that hold them;
+ * pa_bm_fork shares all of them. pa_bm_free lowers the count of each block of
+ * the request; a block at zero goes to the tail of the free list. Requests are
+ * keyed by 64-bit ids; a refused call changes nothing. Not thread-safe: one
+ * manager per host thread, or external locking.
+ *
+ *   pa_bm_create   free_order: a permutation of 0 .. num_blocks-1 giving the
+ *                  initial free list (NULL: ascending); returns NULL on bad
+ *                  arguments or when out of host memory
+ *   pa_bm_block_table / pa_bm_free_list   copy up to `capacity` entries to
+ *                  `out` (may be NULL) and return the full count (-1: unknown)
+ *   pa_bm_slots    slots of positions pos0 .. pos0+count-1 of a request
+ */
+typedef struct pa_block_manager pa_block_manager;
+PA_API pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+PA_API void pa_bm_destroy(pa_block_manager* m);
+PA_API int32_t pa_bm_allocate(pa_block_manager* m, int64_t seq, int64_t num_tokens);
+PA_API int32_t pa_bm_append(pa_block_manager* m, int64_t seq, int64_t* slot, int32_t* cow_src, int32_t* cow_dst);
+PA_API int32_t pa_bm_share_prefix(pa_block_manager* m, int64_t src, int64_t child, int64_t num_tokens);
+PA_API int32_t pa_bm_fork(pa_block_manager* m, int64_t parent, int64_t child);
+PA_API int32_t pa_bm_free(pa_block_manager* m, int64_t seq);
+PA_API int32_t pa_bm_num_free(const pa_block_manager* m);
+PA_API int64_t pa_bm_seq_len(const pa_block_manager* m, int64_t seq);
+PA_API int32_t pa_bm_block_table(const pa_block_manager* m, int64_t seq, int32_t* out, int32_t capacity);
+PA_API int32_t pa_bm_ref_count(const pa_block_manager* m, int32_t block);
+PA_API int32_t pa_bm_free_list(const pa_block_manager* m, int32_t* out, int32_t capacity);
+PA_API int32_t pa_bm_slots(const pa_block_manager* m, int64_t seq, int64_t pos0, int64_t count, int32_t* out);
 
 /*
  * pa_prefill_chunked — a chunk of new query tokens per sequence attends over

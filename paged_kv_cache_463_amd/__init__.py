@@ -7,6 +7,9 @@ the first call does, and raises ``LibraryNotBuilt`` if it is missing.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    BlockManager,
+    copy_blocks,
+    swap_blocks,
     LibraryNotBuilt,
     PagedAttentionError,
     decode,
@@ -18,4 +21,5 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
-           "prefill_chunked", "lib", "LIB_PATH", "LibraryNotBuilt", "PagedAttentionError"]
+           "prefill_chunked", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
+           "LibraryNotBuilt", "PagedAttentionError"]

@@ -11,6 +11,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -19,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_PTR", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
                 4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP",
-                7: "PA_ERR_ALIGNMENT"}
+                7: "PA_ERR_ALIGNMENT", 8: "PA_ERR_NO_BLOCKS", 9: "PA_ERR_SEQUENCE"}
+PA_ERR_NO_BLOCKS, PA_ERR_SEQUENCE = 8, 9
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # exported C symbols -> (restype, argtypes)
@@ -35,6 +37,21 @@ SIGNATURES = {
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
+    "pa_copy_blocks": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
+    "pa_swap_blocks": (_i32, [_p, _i64, _p, _i64, _i64, _p, _i64, _p]),
+    "pa_bm_create": (_p, [_i32, _i32, _p]),
+    "pa_bm_destroy": (None, [_p]),
+    "pa_bm_allocate": (_i32, [_p, _i64, _i64]),
+    "pa_bm_append": (_i32, [_p, _i64, _p, _p, _p]),
+    "pa_bm_share_prefix": (_i32, [_p, _i64, _i64, _i64]),
+    "pa_bm_fork": (_i32, [_p, _i64, _i64]),
+    "pa_bm_free": (_i32, [_p, _i64]),
+    "pa_bm_num_free": (_i32, [_p]),
+    "pa_bm_seq_len": (_i64, [_p, _i64]),
+    "pa_bm_block_table": (_i32, [_p, _i64, _p, _i32]),
+    "pa_bm_ref_count": (_i32, [_p, _i32]),
+    "pa_bm_free_list": (_i32, [_p, _p, _i32]),
+    "pa_bm_slots": (_i32, [_p, _i64, _i64, _i64, _p]),
 }
 
 
@@ -174,3 +191,95 @@ def prefill_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Ten
         _ptr(out), _ptr(query), _ptr(cu_q_lens), max_q_len, T, _ptr(k_cache), _ptr(v_cache), bstride,
         nb, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), seq_lens.numel(), hq, hkv, d,
         bs, scale, int(bool(causal)), _dtype(query), _stream(stream)))
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, stream=None) -> None:
+    """Copy-on-write on the device: block ``dst`` of both pools becomes block ``src`` for each
+    ``(src, dst)`` row of ``pairs`` (int32 ``[n, 2]`` on the device)."""
+    nb, bs, hkv, d, bstride = _pool_dims(k_cache)
+    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
+    _i32_tensor(pairs, "pairs")
+    _require(pairs.dim() == 2 and pairs.shape[1] == 2 and pairs.is_cuda, "pairs must be [n, 2] on the device")
+    _check("pa_copy_blocks", lib().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), bstride, nb, hkv, d, _dtype(k_cache),
+        _ptr(pairs) if pairs.numel() else None, pairs.shape[0], _stream(stream)))
+
+
+def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor, pairs, stream=None) -> None:
+    """Move whole blocks between pools (device or pinned host): block ``dst`` of ``dst_pool``
+    becomes block ``src`` of ``src_pool`` for each ``(src, dst)`` pair (host int64 ``[n, 2]``)."""
+    _require(dst_pool.shape[1:] == src_pool.shape[1:] and dst_pool.dtype == src_pool.dtype, "pools differ")
+    _require(dst_pool.is_contiguous() and src_pool.is_contiguous(), "pools must be contiguous")
+    arr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+    block_bytes = dst_pool[0].numel() * dst_pool.element_size()
+    _check("pa_swap_blocks", lib().pa_swap_blocks(
+        _ptr(dst_pool), dst_pool.shape[0], _ptr(src_pool), src_pool.shape[0], block_bytes,
+        arr.ctypes.data_as(ctypes.c_void_p) if arr.size else None, arr.shape[0], _stream(stream)))
+
+
+class BlockManager:
+    """Host block manager of the library (share counts, head-of-free-list allocation,
+    copy-on-write on append); every call goes to the C ABI ``pa_bm_*``."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, free_order=None):
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            _require(order.size == num_blocks, "free_order must list every block once")
+        self._order = order
+        self._h = lib().pa_bm_create(num_blocks, block_size,
+                                     order.ctypes.data_as(ctypes.c_void_p) if order is not None else None)
+        if not self._h:
+            raise ValueError("pa_bm_create refused its arguments")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pa_bm_destroy(h)
+
+    def allocate(self, seq: int, num_tokens: int) -> None:
+        _check("pa_bm_allocate", lib().pa_bm_allocate(self._h, seq, num_tokens))
+
+    def append(self, seq: int):
+        """One token: returns (slot, (cow_src, cow_dst) or None)."""
+        slot, s, d = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_append", lib().pa_bm_append(self._h, seq, ctypes.byref(slot), ctypes.byref(s),
+                                                  ctypes.byref(d)))
+        return slot.value, (None if s.value < 0 else (s.value, d.value))
+
+    def share_prefix(self, src: int, child: int, num_tokens: int) -> None:
+        _check("pa_bm_share_prefix", lib().pa_bm_share_prefix(self._h, src, child, num_tokens))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, parent, child))
+
+    def free(self, seq: int) -> None:
+        _check("pa_bm_free", lib().pa_bm_free(self._h, seq))
+
+    def num_free(self) -> int:
+        return lib().pa_bm_num_free(self._h)
+
+    def seq_len(self, seq: int) -> int:
+        return lib().pa_bm_seq_len(self._h, seq)
+
+    def block_table(self, seq: int) -> list:
+        n = lib().pa_bm_block_table(self._h, seq, None, 0)
+        _require(n >= 0, f"unknown sequence {seq}")
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        lib().pa_bm_block_table(self._h, seq, out.ctypes.data_as(ctypes.c_void_p), n)
+        return out[:n].tolist()
+
+    def ref_count(self, block: int) -> int:
+        return lib().pa_bm_ref_count(self._h, block)
+
+    def free_list(self) -> list:
+        n = lib().pa_bm_free_list(self._h, None, 0)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        lib().pa_bm_free_list(self._h, out.ctypes.data_as(ctypes.c_void_p), n)
+        return out[:n].tolist()
+
+    def slots(self, seq: int, pos0: int, count: int) -> list:
+        out = np.zeros(max(count, 1), dtype=np.int32)
+        _check("pa_bm_slots", lib().pa_bm_slots(self._h, seq, pos0, count, out.ctypes.data_as(ctypes.c_void_p)))
+        return out[:count].tolist()

@@ -1,0 +1,54 @@
+// copy_blocks: the device half of copy-on-write. Page "vLLM 原理与源码阅读"
+// (PagedAttention 显存管理 → Block 管理器) shares a prompt prefix's physical
+// blocks between requests and copies a shared block only when one request has
+// to write into it; the block manager decides which (source, destination)
+// pairs need a copy, and this kernel makes the copies for K and V before the
+// new tokens are scattered.
+//
+// Mapping: one 256-thread workgroup per (pair, pool); a block's own rows
+// (16 * num_kv_heads * head_dim elements) are moved as raw 16-byte chunks,
+// four loads in flight per thread before their stores, so the copy is
+// bit-exact for every dtype. HBM-bound: 2 * block_bytes read and written per
+// pair. Pairs with an index outside the pool are skipped.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads)
+void copy_blocks_kernel(BlockCopyParams p) {
+  const int64_t i = blockIdx.x;
+  // the pair is uniform over the workgroup: scalar loads through the constant
+  // address space (the table is never written by the kernel)
+  const __attribute__((address_space(4))) int32_t* pr =
+      (const __attribute__((address_space(4))) int32_t*)(p.pairs + 2 * i);
+  const int64_t src = pr[0], dst = pr[1];
+  if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+  char* pool = static_cast<char*>(blockIdx.y == 0 ? p.k_cache : p.v_cache);
+  const char* s = pool + src * p.block_stride_bytes;
+  char* d = pool + dst * p.block_stride_bytes;
+  const int64_t chunks = p.block_bytes >> 4;
+  for (int64_t c0 = threadIdx.x; c0 < chunks; c0 += kCopyThreads * kCopyUnroll) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kCopyThreads;
+      if (c < chunks) v[u] = load16(s + 16 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kCopyThreads;
+      if (c < chunks) *reinterpret_cast<u32x4*>(d + 16 * c) = v[u];
+    }
+  }
+}
+
+hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)p.num_pairs, 2), dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

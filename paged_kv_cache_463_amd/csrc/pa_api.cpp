@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 200;  // 0.2.0
 
 int elem_bytes(int32_t dtype) {
   switch (dtype) {
@@ -94,6 +94,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-KV workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch error";
     case PA_ERR_ALIGNMENT: return "PA_ERR_ALIGNMENT: pointer or stride not 16-byte aligned";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks";
+    case PA_ERR_SEQUENCE: return "PA_ERR_SEQUENCE: unknown request id, or one already in use";
     default: return "unknown pa_status_t";
   }
 }
@@ -129,6 +131,53 @@ int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_toke
   p.num_tokens = num_tokens;
   p.row_bytes = (int32_t)(row * e);
   return hip_status(pa::launch_reshape_and_cache(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_stride, int64_t num_blocks,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype, const int32_t* pairs,
+                       int64_t num_pairs, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  const int64_t block_elems = (int64_t)16 * num_kv_heads * head_dim;
+  if (block_stride < block_elems || num_pairs > 0x7FFFFFFF) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (block_stride * e) % 16 != 0 || (block_elems * e) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::BlockCopyParams p{};
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride * e;
+  p.num_blocks = num_blocks;
+  p.block_bytes = block_elems * e;
+  p.pairs = pairs;
+  p.num_pairs = num_pairs;
+  return hip_status(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_swap_blocks(void* dst_pool, int64_t dst_blocks, const void* src_pool, int64_t src_blocks,
+                       int64_t block_bytes, const int64_t* pairs, int64_t num_pairs, void* stream) {
+  if (num_pairs < 0 || dst_blocks < 0 || src_blocks < 0 || block_bytes <= 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_pool || !src_pool || !pairs) return PA_ERR_NULL_PTR;
+  for (int64_t i = 0; i < num_pairs; ++i) {         // check everything before moving anything
+    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return PA_ERR_SHAPE;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int64_t i = 0;
+  while (i < num_pairs) {                           // merge runs of consecutive pairs
+    const int64_t s0 = pairs[2 * i], d0 = pairs[2 * i + 1];
+    int64_t n = 1;
+    while (i + n < num_pairs && pairs[2 * (i + n)] == s0 + n && pairs[2 * (i + n) + 1] == d0 + n) ++n;
+    const hipError_t e = hipMemcpyAsync(static_cast<char*>(dst_pool) + d0 * block_bytes,
+                                        static_cast<const char*>(src_pool) + s0 * block_bytes,
+                                        (size_t)(n * block_bytes), hipMemcpyDefault, st);
+    if (e != hipSuccess) return PA_ERR_HIP;
+    i += n;
+  }
+  return PA_OK;
 }
 
 int32_t pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -67,7 +67,18 @@ struct PrefillParams {
   float scale;
 };
 
+struct BlockCopyParams {
+  void* k_cache;
+  void* v_cache;
+  int64_t block_stride_bytes;
+  int64_t num_blocks;
+  int64_t block_bytes;          // 16 * num_kv_heads * head_dim * element bytes
+  const int32_t* pairs;         // [num_pairs][2] (source, destination), device
+  int64_t num_pairs;
+};
+
 hipError_t launch_reshape_and_cache(const ScatterParams& p, hipStream_t s);
+hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
