@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "splitkv": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h"],
+    "copy_blocks": ["block_copy.hip", "pa_device.h", "pa_launch.h"],
 }
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6    # dense, 256 CUs at 2.4 GHz
@@ -51,6 +52,11 @@ WORKLOADS = {
     "chunked_prefill_bf16_16x2048p512": ("chunked_prefill_bf16", "prefill"),
 }
 DEFAULT_WORKLOAD = "llama2_7b_fp16_decode_b64"
+# block movement: name -> (pool blocks, kv heads, head_dim, copy pairs, swap blocks)
+BLOCK_WORKLOADS = {
+    "cow_copy_bf16_2048x32k": (8192, 8, 128, 2048, 512),
+}
+COPY_METRIC = "copy-on-write block copy: GB/s, % of MI355X HBM peak, blocks/s"
 
 
 # ----------------------------------------------------------------------------
@@ -245,12 +251,87 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
 
 
 # ----------------------------------------------------------------------------
+def bench_block_copy(args) -> int:
+    """pa_copy_blocks over a batch of copy-on-write pairs (one launch = one step), plus the
+    device <-> pinned-host swap rates of pa_swap_blocks (copy engine, host-link bound)."""
+    import torch
+    import paged_kv_cache_463_amd as P
+    from oracle import block_manager as OBM
+    nb, hkv, d, npairs, nswap = BLOCK_WORKLOADS[args.workload]
+    rng = np.random.default_rng(23)
+    shape = (nb, 16, hkv, d)
+    base = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+    kp = [base.cuda() for _ in range(args.layers)]
+    vp = [(-base).cuda() for _ in range(args.layers)]
+    perm = rng.permutation(nb)
+    pairs_np = np.stack([perm[:npairs], perm[npairs:2 * npairs]], axis=1).astype(np.int32)
+    pairs = torch.from_numpy(pairs_np).cuda()
+    block_bytes = 16 * hkv * d * 2
+    alg = npairs * 2 * block_bytes * 2                  # K and V, read and write
+    for i in range(args.warmup):
+        P.copy_blocks(kp[i % args.layers], vp[i % args.layers], pairs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        P.copy_blocks(kp[i % args.layers], vp[i % args.layers], pairs)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    achieved = alg / (us * 1e-6) / 1e9
+    # swap: nswap blocks of one pool out to pinned host memory and back, timed with events
+    host = torch.empty((nswap,) + shape[1:], dtype=torch.bfloat16, pin_memory=True)
+    sw_out = [(int(b), i) for i, b in enumerate(perm[:nswap])]
+    sw_in = [(i, int(b)) for i, b in enumerate(perm[:nswap])]
+    rates = {}
+    for name, (dst, src, prs) in {"out": (host, kp[0], sw_out), "in": (kp[0], host, sw_in)}.items():
+        P.swap_blocks(dst, src, prs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            P.swap_blocks(dst, src, prs)
+        b.record(stream)
+        torch.cuda.synchronize()
+        rates[name] = 5 * nswap * block_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
+    res = {"metric": COPY_METRIC, "value": npairs * args.steps / elapsed, "unit": "blocks/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) pools, random disjoint copy pairs)",
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBPS,
+                        "traffic": stored_traffic(args.workload, "copy_blocks", 0)},
+           "copy_us_per_launch": us, "algorithmic_bytes_per_launch": alg,
+           "swap_gb_per_s": {"device_to_host": rates["out"], "host_to_device": rates["in"],
+                             "blocks": nswap, "block_bytes": block_bytes},
+           "config": {"workload": args.workload, "kernel": "copy_blocks", "pool_blocks": nb,
+                      "num_kv_heads": hkv, "head_dim": d, "block_size": 16, "copy_pairs": npairs,
+                      "pool_replicas": args.layers}}
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+    else:
+        kh, vh = base.float().numpy(), (-base).float().numpy()
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 5.0):
+            OBM.copy_blocks(kh, vh, pairs_np[:256].tolist())
+            done += 256
+        secs = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done / secs, "unit": "blocks/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} block copies (256-pair batches of the same pairs on "
+                                         f"fp32 copies of the pools), NumPy, {secs:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--kernel", default=None, choices=["decode", "splitkv", "prefill"],
                     help="attention entry point (default: the workload's)")
     ap.add_argument("--partition", type=int, default=512, help="split-KV partition size (tokens)")
@@ -269,6 +350,8 @@ def main(argv=None) -> int:
     import torch
     import workloads as W
 
+    if args.workload in BLOCK_WORKLOADS:
+        return bench_block_copy(args)
     gen_key, call = WORKLOADS[args.workload]
     call = args.kernel or call
     t_gen = time.perf_counter()

@@ -51,4 +51,36 @@ hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// swap_blocks: whole blocks between two pools that the device can address -
+// device memory, or pinned host memory mapped into the device's address space
+// (the CPU swap space of page "vLLM推理引擎深度实战" §5.3). One launch moves up to
+// kSwapChunk pairs, carried in the kernel arguments; one workgroup per pair,
+// 16-byte chunks, four in flight per thread. The host side checks every pair
+// and the pools' accessibility before launching.
+__global__ __launch_bounds__(kCopyThreads)
+void swap_blocks_kernel(SwapChunk c) {
+  const int i = blockIdx.x;
+  const char* s = static_cast<const char*>(c.src) + (int64_t)c.pairs[i][0] * c.block_bytes;
+  char* d = static_cast<char*>(c.dst) + (int64_t)c.pairs[i][1] * c.block_bytes;
+  const int64_t chunks = c.block_bytes >> 4;
+  for (int64_t c0 = threadIdx.x; c0 < chunks; c0 += kCopyThreads * kCopyUnroll) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t k = c0 + (int64_t)u * kCopyThreads;
+      if (k < chunks) v[u] = load16(s + 16 * k);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t k = c0 + (int64_t)u * kCopyThreads;
+      if (k < chunks) *reinterpret_cast<u32x4*>(d + 16 * k) = v[u];
+    }
+  }
+}
+
+hipError_t launch_swap_chunk(const SwapChunk& c, hipStream_t s) {
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)c.num_pairs), dim3(kCopyThreads), 0, s, c);
+  return hipGetLastError();
+}
+
 }  // namespace pa

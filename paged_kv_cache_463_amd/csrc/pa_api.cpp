@@ -2,6 +2,8 @@
 // Declarations, layouts and error behaviour are documented in include/pa.h.
 // Validation touches no HIP API, so every error path returns before any
 // device work is enqueued.
+#include <algorithm>
+
 #include "pa.h"
 
 #include <hip/hip_runtime.h>
@@ -26,6 +28,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// The address under which the device reaches `p`, or nullptr when it cannot:
+// device and managed memory as they are, pinned host memory through its mapped
+// device address; pageable host memory is unknown to the runtime (the query
+// fails, and its error is cleared so that it cannot surface later).
+const void* device_view(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged || a.isManaged) return p;
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    const char* base_h = static_cast<const char*>(a.hostPointer ? a.hostPointer : p);
+    return static_cast<const char*>(a.devicePointer) + (static_cast<const char*>(p) - base_h);
+  }
+  return nullptr;
+}
+void* device_view(void* p) { return const_cast<void*>(device_view(static_cast<const void*>(p))); }
 
 // Checks shared by the attention entry points.
 int32_t check_attention_common(const void* out, const void* query, const void* k_cache,
@@ -166,6 +187,27 @@ int32_t pa_swap_blocks(void* dst_pool, int64_t dst_blocks, const void* src_pool,
     if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return PA_ERR_SHAPE;
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // both pools addressable by the device (device memory, or pinned host memory
+  // mapped into its address space): the swap kernel moves every pair in a few
+  // launches; otherwise the copy engine moves runs of consecutive pairs
+  void* dview = device_view(dst_pool);
+  const void* sview = device_view(src_pool);
+  if (dview && sview && block_bytes % 16 == 0 && aligned16(dview) && aligned16(sview) &&
+      dst_blocks <= 0x7FFFFFFF && src_blocks <= 0x7FFFFFFF) {
+    pa::SwapChunk c{};
+    c.dst = dview;
+    c.src = sview;
+    c.block_bytes = block_bytes;
+    for (int64_t i0 = 0; i0 < num_pairs; i0 += pa::kSwapChunk) {
+      c.num_pairs = (int32_t)std::min<int64_t>(pa::kSwapChunk, num_pairs - i0);
+      for (int32_t k = 0; k < c.num_pairs; ++k) {
+        c.pairs[k][0] = (int32_t)pairs[2 * (i0 + k)];
+        c.pairs[k][1] = (int32_t)pairs[2 * (i0 + k) + 1];
+      }
+      if (pa::launch_swap_chunk(c, st) != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+  }
   int64_t i = 0;
   while (i < num_pairs) {                           // merge runs of consecutive pairs
     const int64_t s0 = pairs[2 * i], d0 = pairs[2 * i + 1];

@@ -78,7 +78,17 @@ struct BlockCopyParams {
 };
 
 hipError_t launch_reshape_and_cache(const ScatterParams& p, hipStream_t s);
+constexpr int kSwapChunk = 240;              // pairs per swap launch (kernel-argument space)
+struct SwapChunk {
+  void* dst;                    // both pools addressable by the device
+  const void* src;
+  int64_t block_bytes;          // a multiple of 16
+  int32_t num_pairs;            // 1 .. kSwapChunk
+  int32_t pairs[kSwapChunk][2]; // (source, destination), checked on the host
+};
+
 hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s);
+hipError_t launch_swap_chunk(const SwapChunk& c, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);

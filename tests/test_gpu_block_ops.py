@@ -83,6 +83,19 @@ def test_swap_blocks_out_and_in_bit_exact():
     assert host_bits(back, "bf16").tobytes() == before.tobytes()   # nothing moved
 
 
+def test_swap_blocks_pageable_host_pool():
+    """Host memory the device cannot address (not pinned) goes through the copy engine."""
+    rng = np.random.default_rng(19)
+    dh, dd = random_pool(rng, 12, 2, 64, "f16")
+    host = torch.zeros((6, 16, 2, 64), dtype=torch.float16)              # pageable
+    pairs = [(2, 0), (3, 1), (11, 5), (0, 3)]
+    say("case: swap_blocks device -> pageable host")
+    P.swap_blocks(host, dd, pairs)
+    torch.cuda.synchronize()
+    want = OBM.swap_blocks(np.zeros((6, 16, 2, 64), np.uint16), dh, pairs)
+    assert host.view(torch.int16).numpy().view(np.uint16).tobytes() == want.tobytes()
+
+
 def test_copy_on_write_decode_step():
     """Request 1 shares request 0's first 40 tokens (a partly filled third block); both then
     append a token. The manager asks for one copy, the copy and the scatter run on the device,
