@@ -30,6 +30,14 @@ new block on append, copy-on-write of a shared block before a write (pages
 "vLLM推理引擎深度解析" §三, "vLLM 原理与源码阅读" Block 管理器, "vLLM推理引擎深度实战"
 §5.3); its pins are in ``tests/test_block_manager_oracle.py``.
 
+``fp8`` (imported as a module) holds the e4m3 KV cache: the format's values,
+round-to-nearest-even quantisation with one float32 scale per kv head, the
+quantising cache write and decode over the dequantised cache (the pages only
+list FP8 among the supported quantisation schemes, page "vLLM推理引擎深度实战",
+introduction; the format is the OCP 8-bit floating point E4M3); its pins, in
+``tests/test_fp8_oracle.py``, compare it with torch's float8_e4m3fn conversion,
+closed forms and the 16-bit oracle.
+
 Parity pins: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` against something other than itself (torch's
 fp64 ``scaled_dot_product_attention``, 40-digit ``decimal`` brute force, closed
@@ -38,6 +46,7 @@ and mutation tests plant mistakes in this oracle to show that the pins catch
 them. No function is "parity unpinned".
 """
 from . import block_manager  # noqa: F401
+from . import fp8  # noqa: F401
 from .paged_attention import (  # noqa: F401
     to_f64,
     scatter,
