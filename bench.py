@@ -36,6 +36,8 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_463_amd", "csrc")
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "splitkv": ["decode.hip", "pa_device.h", "pa_launch.h"],
+    "decode_fp8": ["decode.hip", "pa_device.h", "pa_launch.h"],
+    "splitkv_fp8": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h"],
     "copy_blocks": ["block_copy.hip", "pa_device.h", "pa_launch.h"],
 }
@@ -50,6 +52,10 @@ WORKLOADS = {
     "long_ctx_bf16_splitkv_b8": ("long_context_bf16", "splitkv"),
     "tiny_fp32_decode_b4": ("tiny", "decode"),
     "chunked_prefill_bf16_16x2048p512": ("chunked_prefill_bf16", "prefill"),
+    # the same decode workloads over an FP8 (e4m3) KV cache
+    "llama2_7b_fp8kv_decode_b64": ("llama2_7b_fp16", "decode_fp8"),
+    "llama3_8b_gqa_fp8kv_decode_b256": ("llama3_8b_gqa_bf16", "decode_fp8"),
+    "long_ctx_fp8kv_splitkv_b8": ("long_context_bf16", "splitkv_fp8"),
 }
 DEFAULT_WORKLOAD = "llama2_7b_fp16_decode_b64"
 # block movement: name -> (pool blocks, kv heads, head_dim, copy pairs, swap blocks)
@@ -62,12 +68,17 @@ COPY_METRIC = "copy-on-write block copy: GB/s, % of MI355X HBM peak, blocks/s"
 # ----------------------------------------------------------------------------
 # algorithmic work (what the operation must touch, independent of the kernel)
 # ----------------------------------------------------------------------------
-def decode_bytes(case, unique: bool) -> int:
+def kv_elem_bytes(case, call: str) -> int:
+    import workloads as W
+    return 1 if call.endswith("_fp8") else W.ELEM_BYTES[case.dtype]
+
+
+def decode_bytes(case, unique: bool, call: str = "decode") -> int:
     """KV rows of every cached token (shared prefix blocks once if ``unique``),
     plus query, output, the table entries read and the lengths."""
     import workloads as W
     e = W.ELEM_BYTES[case.dtype]
-    row = 2 * case.num_kv_heads * case.head_dim * e          # K and V of one token, all kv heads
+    row = 2 * case.num_kv_heads * case.head_dim * kv_elem_bytes(case, call)   # K and V of one token
     tokens = int(case.context_lens.astype(np.int64).sum())
     if unique and case.shared_blocks:
         tokens -= (len(case.sharers) - 1) * len(case.shared_blocks) * W.BLOCK_SIZE
@@ -76,20 +87,21 @@ def decode_bytes(case, unique: bool) -> int:
     return tokens * row + qo + tables
 
 
-def kv_bytes(case, unique: bool) -> int:
+def kv_bytes(case, unique: bool, call: str = "decode") -> int:
     import workloads as W
-    e = W.ELEM_BYTES[case.dtype]
+    e = kv_elem_bytes(case, call)
     tokens = int(case.context_lens.astype(np.int64).sum())
     if unique and getattr(case, "shared_blocks", None):
         tokens -= (len(case.sharers) - 1) * len(case.shared_blocks) * W.BLOCK_SIZE
     return tokens * 2 * case.num_kv_heads * case.head_dim * e
 
 
-def scatter_bytes(case) -> int:
+def scatter_bytes(case, call: str = "decode") -> int:
     import workloads as W
     e = W.ELEM_BYTES[case.dtype]
     n = len(case.slot_mapping)
-    return 2 * 2 * n * case.num_kv_heads * case.head_dim * e + 4 * n     # read + write, K and V
+    row = case.num_kv_heads * case.head_dim
+    return 2 * n * row * (e + kv_elem_bytes(case, call)) + 4 * n         # read + write, K and V
 
 
 def prefill_flops(case) -> int:
@@ -122,7 +134,7 @@ def stored_traffic(workload: str, call: str, partition: int):
         rec = json.load(fh)
     if rec.get("kernel_source_sha256") != kernel_source_sha256(call):
         return None
-    if call == "splitkv" and rec.get("partition_size") != partition:
+    if call.startswith("splitkv") and rec.get("partition_size") != partition:
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -147,7 +159,14 @@ class Runner:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
-        k0, v0 = dev(case.k_pool), dev(case.v_pool)
+        self.fp8 = call.endswith("_fp8")
+        if self.fp8:                                # e4m3 codes and per-head scales
+            f = W.fp8_pools(case, 0)
+            k0, v0 = torch.from_numpy(f.k_pool).cuda(), torch.from_numpy(f.v_pool).cuda()
+            self.ks, self.vs = torch.from_numpy(f.k_scale).cuda(), torch.from_numpy(f.v_scale).cuda()
+            self.fp8_host = f
+        else:
+            k0, v0 = dev(case.k_pool), dev(case.v_pool)
         self.kp = [k0] + [k0.clone() for _ in range(layers - 1)]
         self.vp = [v0] + [v0.clone() for _ in range(layers - 1)]
         self.q = dev(case.query)
@@ -168,7 +187,11 @@ class Runner:
         assert self.q.dtype == dt
 
     def scatter(self, layer: int):
-        self.P.reshape_and_cache(self.kn, self.vn, self.kp[layer], self.vp[layer], self.slots)
+        if self.fp8:
+            self.P.reshape_and_cache_fp8(self.kn, self.vn, self.kp[layer], self.vp[layer], self.slots,
+                                         self.ks, self.vs)
+        else:
+            self.P.reshape_and_cache(self.kn, self.vn, self.kp[layer], self.vp[layer], self.slots)
 
     def attend(self, layer: int):
         c, P = self.case, self.P
@@ -177,6 +200,12 @@ class Runner:
         elif self.call == "splitkv":
             P.decode_splitkv(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale,
                              self.mcl, self.partition, self.ws)
+        elif self.call == "decode_fp8":
+            P.decode_fp8(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale,
+                         self.ks, self.vs)
+        elif self.call == "splitkv_fp8":
+            P.decode_splitkv_fp8(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale,
+                                 self.ks, self.vs, self.mcl, self.partition, self.ws)
         else:
             P.prefill_chunked(self.out, self.q, self.cu, self.max_q, self.kp[layer], self.vp[layer], self.bt,
                               self.lens, c.scale, True)
@@ -215,7 +244,12 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    kp, vp = oracle.scatter(case.k_pool, case.v_pool, case.k_new, case.v_new, case.slot_mapping)
+    if r.fp8:
+        f = r.fp8_host
+        kp, vp = oracle.fp8.scatter_fp8(f.k_pool, f.v_pool, case.k_new, case.v_new, case.slot_mapping,
+                                        f.k_scale, f.v_scale, case.dtype)
+    else:
+        kp, vp = oracle.scatter(case.k_pool, case.v_pool, case.k_new, case.v_new, case.slot_mapping)
     gpu_out = r.out.float().cpu().double().numpy()
     order = np.random.default_rng(0).permutation(case.num_seqs)
     t0 = time.perf_counter()
@@ -230,6 +264,12 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
                 q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
                 err = max(err, float(np.abs(ref[q0:q1] - gpu_out[q0:q1]).max()))
                 units += q1 - q0
+            elif r.fp8:
+                ref = oracle.fp8.paged_decode_fp8(case.query[[b]], kp, vp, case.block_tables[[b]],
+                                                  case.context_lens[[b]], case.scale, f.k_scale, f.v_scale,
+                                                  case.num_kv_heads, case.dtype)
+                err = max(err, float(np.abs(ref[0] - gpu_out[b]).max()))
+                units += 1
             else:
                 ref = oracle.paged_decode(case.query[[b]], kp, vp, case.block_tables[[b]], case.context_lens[[b]],
                                           case.scale, case.num_kv_heads, case.dtype)
@@ -332,7 +372,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
-    ap.add_argument("--kernel", default=None, choices=["decode", "splitkv", "prefill"],
+    ap.add_argument("--kernel", default=None,
+                    choices=["decode", "splitkv", "prefill", "decode_fp8", "splitkv_fp8"],
                     help="attention entry point (default: the workload's)")
     ap.add_argument("--partition", type=int, default=512, help="split-KV partition size (tokens)")
     ap.add_argument("--layers", type=int, default=4, help="KV pool replicas rotated over steps")
@@ -390,8 +431,8 @@ def main(argv=None) -> int:
         res["prefill_causal_flops_per_step"] = flops
         cfg.update({"prior_tokens": int(case.prior_lens[0]), "chunk_tokens": int(case.q_lens[0]), "causal": True})
     else:
-        ab_unique = decode_bytes(case, unique=True)
-        kv_logical, kv_unique = kv_bytes(case, False), kv_bytes(case, True)
+        ab_unique = decode_bytes(case, True, call)
+        kv_logical, kv_unique = kv_bytes(case, False, call), kv_bytes(case, True, call)
         res.update({"value": case.num_seqs * args.steps / elapsed, "unit": "seq-steps/s"})
         achieved = ab_unique / (attn_us * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -403,10 +444,14 @@ def main(argv=None) -> int:
         res["algorithmic_bytes_per_launch"] = ab_unique
         cfg.update({"context_tokens": int(case.context_lens.astype(np.int64).sum()),
                     "max_context_len": case.max_context_len})
-        if call == "splitkv":
+        if call.startswith("splitkv"):
             cfg["partition_size"] = args.partition
+        if call.endswith("_fp8"):
+            cfg["kv_cache_dtype"] = "fp8_e4m3"
+            res["data"] = ("synthetic (seeded N(0,1) queries and new K/V, uniform e4m3 cache codes with "
+                           "per-head scales, shuffled physical blocks)")
     res["attention_us_per_launch"] = attn_us
-    res["scatter_bytes_per_step"] = scatter_bytes(case)
+    res["scatter_bytes_per_step"] = scatter_bytes(case, call)
     res["config"] = cfg
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(case, call, r, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -14,8 +14,9 @@
  *        (one block table per request, 16 tokens per block by default,
  *        copy-on-write for shared prefix blocks).
  *   [P3] "vLLM推理引擎深度实战", §1.2 PagedAttention原理 (BLOCK_SIZE = 16,
- *        a block holds K and V of its tokens for all heads) and §5.3
- *        推理优化配置 (the chunked-prefill switch).
+ *        a block holds K and V of its tokens for all heads), §5.3
+ *        推理优化配置 (the chunked-prefill switch) and the introduction (FP8
+ *        among the supported quantisation schemes).
  *
  * Common conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -164,6 +165,67 @@ PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cac
                           int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
                           int32_t max_context_len, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV cache. [P3] (introduction) lists FP8 among the quantisation schemes
+ * the engine supports and gives no format; the format here is the OCP 8-bit
+ * floating point E4M3 ("e4m3fn": bias 7, 3 mantissa bits, subnormals, no
+ * infinities, NaN = S.1111.111, largest finite 448), one byte per element, in
+ * the pool layout above with block_stride counted in bytes. Each kv head h has
+ * two float32 scales: a stored code c stands for K = value(c) * k_scale[h]
+ * (V likewise with v_scale[h]). k_scale and v_scale are DEVICE float32 arrays
+ * [num_kv_heads], finite and > 0 (a precondition, not checked).
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 — pa_reshape_and_cache into an FP8 cache. Element
+ * x of head h is stored as the e4m3 code nearest to fl32(x / scale[h]) (x
+ * widened exactly to float32, one correctly rounded float32 division; ties to
+ * the even mantissa; finite values beyond +-448 and infinities saturate to
+ * +-448; NaN stays NaN; the sign of zero is kept).
+ *
+ *   key, value       [num_tokens][num_kv_heads][head_dim] of `dtype` (any
+ *                    pa_dtype_t), row t at element t * kv_token_stride
+ *   k_cache, v_cache FP8 pools, block_stride in bytes (>= 16*H_kv*D, a
+ *                    multiple of 16)
+ *   k_scale, v_scale float32 [num_kv_heads], device
+ * Other arguments, slot rules and errors as pa_reshape_and_cache.
+ */
+PA_API int32_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                                 void* k_cache, void* v_cache, int64_t block_stride,
+                                 int64_t num_blocks, const int32_t* slot_mapping, int64_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 const float* k_scale, const float* v_scale, int32_t dtype,
+                                 void* stream);
+
+/*
+ * pa_decode_fp8 — pa_decode over an FP8 cache: the same attention with K and
+ * V dequantised as above. `dtype` (PA_DTYPE_F16 or PA_DTYPE_BF16) is the type
+ * of query and out; cache codes are widened to it exactly, products
+ * accumulate in fp32, k_scale[h] joins the score scale and v_scale[h] the
+ * output. block_stride is in bytes. Returns PA_ERR_DTYPE for PA_DTYPE_F32.
+ */
+PA_API int32_t pa_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                      int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                      int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, const float* k_scale, const float* v_scale,
+                      int32_t dtype, void* stream);
+
+/*
+ * pa_decode_splitkv_fp8 — pa_decode_splitkv over an FP8 cache (dequantised
+ * as in pa_decode_fp8). Workspace size from pa_decode_splitkv_workspace_bytes,
+ * which does not depend on the cache type; other arguments as
+ * pa_decode_splitkv, block_stride in bytes.
+ */
+PA_API int32_t pa_decode_splitkv_fp8(void* out, const void* query, const void* k_cache,
+                              const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float scale, const float* k_scale, const float* v_scale,
+                              int32_t dtype, int32_t max_context_len, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_copy_blocks — the device half of copy-on-write ([P2] Block 管理器: requests

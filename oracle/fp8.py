@@ -15,8 +15,10 @@ they give no format, scale or rounding. The readings taken here:
 * writing a token quantises each element ``x`` as ``y = fl32(x / scale)`` (x
   widened exactly to float32, one correctly rounded float32 division), then
   rounds ``y`` to the nearest e4m3 value, ties to the even mantissa; finite
-  values beyond +-448 (and infinities) saturate to +-448; NaN stays NaN; the
-  sign of zero is kept;
+  values beyond +-448 (and infinities) saturate to +-448; NaN stays NaN with
+  its sign bit (the sign a division leaves on a NaN is not fixed by IEEE 754,
+  so only NaN inputs of positive sign have a defined code); the sign of zero is
+  kept;
 * attention reads the dequantised cache: ``K = value(code) * k_scale[h]``,
   ``V = value(code) * v_scale[h]``, and is otherwise the attention of
   ``paged_attention``.
@@ -64,9 +66,9 @@ def _round_half_even(x: float) -> int:
 
 def e4m3_code(y: float) -> int:
     """Nearest e4m3 code of one value (ties to even mantissa, saturating to +-448)."""
-    if math.isnan(y):
-        return 0x7F
     sign = 0x80 if math.copysign(1.0, y) < 0 else 0
+    if math.isnan(y):
+        return sign | 0x7F                                # NaN keeps its sign bit
     a = abs(y)
     if a >= E4M3_MAX:                                     # includes infinity
         return sign | 0x7E
@@ -104,11 +106,11 @@ def scatter_fp8(k_pool: np.ndarray, v_pool: np.ndarray, key, value, slot_mapping
     return scatter(k_pool, v_pool, kq, vq, slot_mapping, block_size)
 
 
-def dequantize(pool: np.ndarray, scale) -> np.ndarray:
-    """float64 pool ``[num_blocks, block_size, H_kv, D]``: value(code) * scale[h]."""
+def dequantize(codes: np.ndarray, scale) -> np.ndarray:
+    """float64 ``value(code) * scale[h]`` for codes ``[..., H_kv, D]`` (a pool or gathered rows)."""
     tab = e4m3_table()
     s = np.asarray(scale, np.float32).astype(np.float64)
-    return tab[np.asarray(pool, np.uint8)] * s[None, None, :, None]
+    return tab[np.asarray(codes, np.uint8)] * s[:, None]
 
 
 def paged_decode_fp8(query, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale,
@@ -118,15 +120,13 @@ def paged_decode_fp8(query, k_pool, v_pool, block_tables, context_lens, scale, k
     B, Hq, D = query.shape
     sc = _scale64(scale)
     q64 = to_f64(query, dtype)
-    K64 = dequantize(k_pool, k_scale)
-    V64 = dequantize(v_pool, v_scale)
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(context_lens[b])
         if L == 0:
             continue
-        K = gather(K64, block_tables[b], L, block_size)
-        V = gather(V64, block_tables[b], L, block_size)
+        K = dequantize(gather(k_pool, block_tables[b], L, block_size), k_scale)    # [L, H_kv, D]
+        V = dequantize(gather(v_pool, block_tables[b], L, block_size), v_scale)
         for h in range(Hq):
             g = kv_head_of(h, Hq, num_kv_heads)
             out[b, h] = attend(q64[b, h], K[:, g], V[:, g], sc)

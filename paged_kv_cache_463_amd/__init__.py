@@ -13,13 +13,17 @@ from ._binding import (  # noqa: F401
     LibraryNotBuilt,
     PagedAttentionError,
     decode,
+    decode_fp8,
     decode_splitkv,
+    decode_splitkv_fp8,
     lib,
     prefill_chunked,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     splitkv_workspace_bytes,
 )
 
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
+           "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8",
            "prefill_chunked", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
            "LibraryNotBuilt", "PagedAttentionError"]

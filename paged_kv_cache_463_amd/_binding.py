@@ -37,6 +37,12 @@ SIGNATURES = {
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
+    "pa_reshape_and_cache_fp8": (_i32, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _i32, _i32, _i32, _p, _p,
+                                         _i32, _p]),
+    "pa_decode_fp8": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32,
+                              _p, _p, _i32, _p]),
+    "pa_decode_splitkv_fp8": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+                                      _f32, _p, _p, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_copy_blocks": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
     "pa_swap_blocks": (_i32, [_p, _i64, _p, _i64, _i64, _p, _i64, _p]),
     "pa_bm_create": (_p, [_i32, _i32, _p]),
@@ -175,6 +181,69 @@ def decode_splitkv(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
         max_context_len, partition_size, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def _fp8_pools(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor):
+    """FP8 pools are uint8 tensors holding e4m3 codes; scales float32 ``[H_kv]``."""
+    _require(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8, "FP8 pools must be uint8 (e4m3 codes)")
+    dims = _pool_dims(k_cache)
+    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _require(t.dtype == torch.float32 and t.is_contiguous() and t.numel() == dims[2],
+                 f"{name} must be contiguous float32 [num_kv_heads]")
+    return dims
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: torch.Tensor,
+                          v_scale: torch.Tensor, stream=None) -> None:
+    """Quantise ``key``/``value`` ``[T, H_kv, D]`` rows to e4m3 with per-head scales and write
+    them into the FP8 pools at ``slot_mapping``."""
+    nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
+    _require(key.shape == value.shape and key.stride() == value.stride(), "key/value differ")
+    _require(key.dim() == 3 and key.stride(2) == 1 and key.stride(1) == d, "key rows must be [H_kv, D] contiguous")
+    _i32_tensor(slot_mapping, "slot_mapping")
+    _require(slot_mapping.numel() == key.shape[0], "slot_mapping length")
+    _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), key.stride(0), _ptr(k_cache), _ptr(v_cache), bstride, nb,
+        _ptr(slot_mapping), key.shape[0], hkv, d, bs, _ptr(k_scale), _ptr(v_scale), _dtype(key),
+        _stream(stream)))
+
+
+def decode_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: torch.Tensor,
+               v_scale: torch.Tensor, stream=None) -> None:
+    """Single-pass paged decode over FP8 pools; ``out``/``query`` ``[B, H_q, D]`` in f16 or bf16."""
+    nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
+    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(context_lens, "context_lens")
+    B, hq, _ = query.shape
+    _check("pa_decode_fp8", lib().pa_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _ptr(k_scale), _ptr(v_scale),
+        _dtype(query), _stream(stream)))
+
+
+def decode_splitkv_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                       k_scale: torch.Tensor, v_scale: torch.Tensor, max_context_len: int,
+                       partition_size: int = 512, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Split-KV decode over FP8 pools (workspace as ``decode_splitkv``)."""
+    nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
+    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(context_lens, "context_lens")
+    B, hq, _ = query.shape
+    need = splitkv_workspace_bytes(B, hq, d, max(max_context_len, 1), partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    _check("pa_decode_splitkv_fp8", lib().pa_decode_splitkv_fp8(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _ptr(k_scale), _ptr(v_scale),
+        _dtype(query), max_context_len, partition_size, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def prefill_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,

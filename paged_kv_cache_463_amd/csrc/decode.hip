@@ -57,6 +57,8 @@
 
 namespace pa {
 
+static_assert(static_cast<int>(DT::FP8) == kKvFp8, "cache type codes agree");
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units: p <= 2^8 between rescales
 
@@ -315,11 +317,22 @@ __global__ void splitkv_reset_kernel(int32_t* ctr) {
   if (threadIdx.x == 0) *ctr = 0;
 }
 
-template <DT dt, int D, int G, int W, bool SPLIT, int NB>
+// A lane's cache slice of one token row: 16 bytes of a 16-bit or fp32 cache,
+// or the 8 bytes of an FP8 cache that hold the same EPL elements.
+template <DT kt> struct KvRaw { using type = u32x4; };
+template <> struct KvRaw<DT::FP8> { using type = u32x2; };
+
+template <DT dt, DT kt, int D, int G, int W, bool SPLIT, int NB>
 __global__ __launch_bounds__(64 * W)
 void decode_kernel(DecodeParams p) {
+  constexpr bool F8 = kt == DT::FP8;        // e4m3 cache, widened to dt on the fly
+  static_assert(F8 || kt == dt, "a 16-bit or fp32 cache has the query's type");
+  static_assert(!F8 || dt != DT::F32, "an fp8 cache is read with 16-bit queries");
+  using KR = typename KvRaw<kt>::type;
   constexpr int E = Elem<dt>::bytes;
+  constexpr int KE = Elem<kt>::bytes;       // cache bytes per element
   constexpr int EPL = 16 / E;               // elements per lane per load
+  constexpr int KB = EPL * KE;              // cache bytes per lane per load
   constexpr int LPR = D / EPL;              // lanes per token row
   constexpr int ROWS = 64 / LPR;            // rows per wave load
   constexpr int TPL = kBlockSize / ROWS;    // tokens per lane per block
@@ -371,9 +384,11 @@ void decode_kernel(DecodeParams p) {
   uint32_t off[TPL];
 #pragma unroll
   for (int j = 0; j < TPL; ++j)
-    off[j] = (uint32_t)((((r + ROWS * j) * p.num_kv_heads + g) * D) * E + c * 16);
+    off[j] = (uint32_t)((((r + ROWS * j) * p.num_kv_heads + g) * D) * KE + c * KB);
 
-  const float sl2 = p.scale * kLog2e;
+  // an fp8 cache stores K / k_scale and V / v_scale per kv head: k_scale folds
+  // into the score scale and v_scale into the output
+  const float sl2 = p.scale * kLog2e * (F8 ? p.k_scale[g] : 1.f);
   // constant address space: the uniform table lookups stay scalar loads even
   // where an asm statement below tells the compiler that memory may change
   const __attribute__((address_space(4))) int32_t* tbl =
@@ -396,25 +411,32 @@ void decode_kernel(DecodeParams p) {
   // drain the prefetch of every block), and re-reading the block a wave has
   // just read is an L2 hit.
   auto block_id = [&](int i) -> int { return tbl[min(i, hi - 1)]; };
-  auto fetch = [&](int bid, u32x4* kd, u32x4* vd) -> bool {
+  auto load_kv = [](const char* a) -> KR {
+    if constexpr (F8) return load8(a);
+    else return load16(a);
+  };
+  auto fetch = [&](int bid, KR* kd, KR* vd) -> bool {
     const bool ok = (bid >= 0) && (bid < p.num_blocks);
     bid = ok ? bid : 0;                      // never address outside the pool
     const char* kb = kc + (int64_t)bid * p.block_stride_bytes;
     const char* vb = vc + (int64_t)bid * p.block_stride_bytes;
 #pragma unroll
-    for (int j = 0; j < TPL; ++j) kd[j] = load16(kb + off[j]);
+    for (int j = 0; j < TPL; ++j) kd[j] = load_kv(kb + off[j]);
 #pragma unroll
-    for (int j = 0; j < TPL; ++j) vd[j] = load16(vb + off[j]);
+    for (int j = 0; j < TPL; ++j) vd[j] = load_kv(vb + off[j]);
     return ok;
   };
 
-  auto process = [&](int i, u32x4* kb, u32x4* vb, bool ok) {
+  auto process = [&](int i, KR* kb, KR* vb, bool ok) {
     float x[TPL];
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
+      u32x4 kw;
+      if constexpr (F8) kw = widen_fp8<dt>(kb[j]);
+      else kw = kb[j];
       float v[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) v[h] = row_dot<dt>(q[h], kb[j]);
+      for (int h = 0; h < G; ++h) v[h] = row_dot<dt>(q[h], kw);
       reduce_scatter<G, LPR>(v);
       x[j] = v[0] * sl2;
     }
@@ -424,12 +446,17 @@ void decode_kernel(DecodeParams p) {
     // instead switch the byte selectors that split V into token pairs to the
     // constant-zero selector, which leaves the loaded registers untouched (no
     // copies, no early wait on the V loads).
+    // An fp8 cache pairs bytes instead: [c j, c j+1, c+1 j, c+1 j+1] for
+    // columns (4i, 4i+1) and (4i+2, 4i+3) of one dword, before widening.
     const int tok0 = i * kBlockSize;
+    constexpr uint32_t kSelLo = F8 ? 0x05010400u : 0x05040100u;   // column 2i of tokens (j, j+1)
+    constexpr uint32_t kSelHi = F8 ? 0x07030602u : 0x07060302u;   // column 2i+1
+    constexpr uint32_t kKeepJ1 = F8 ? 0xFF00FF00u : 0xFFFF0000u;  // selector bytes of token j+1
     uint32_t sel_lo[TPL / 2 > 0 ? TPL / 2 : 1], sel_hi[TPL / 2 > 0 ? TPL / 2 : 1];
 #pragma unroll
     for (int j = 0; j < TPL / 2; ++j) {
-      sel_lo[j] = 0x05040100u;                // column 2i of tokens (j, j+1)
-      sel_hi[j] = 0x07060302u;                // column 2i+1
+      sel_lo[j] = kSelLo;
+      sel_hi[j] = kSelHi;
     }
     if (!ok || tok0 + kBlockSize > L) {      // uniform: only a sequence's last block
 #pragma unroll
@@ -439,11 +466,11 @@ void decode_kernel(DecodeParams p) {
           if constexpr (dt == DT::F32) {
             vb[j] = u32x4{0u, 0u, 0u, 0u};
           } else if ((j & 1) == 0) {         // byte selector 12 yields 0x00
-            sel_lo[j / 2] = (sel_lo[j / 2] & 0xFFFF0000u) | 0x0C0Cu;
-            sel_hi[j / 2] = (sel_hi[j / 2] & 0xFFFF0000u) | 0x0C0Cu;
+            sel_lo[j / 2] = (sel_lo[j / 2] & kKeepJ1) | (0x0C0C0C0Cu & ~kKeepJ1);
+            sel_hi[j / 2] = (sel_hi[j / 2] & kKeepJ1) | (0x0C0C0C0Cu & ~kKeepJ1);
           } else {
-            sel_lo[j / 2] = (sel_lo[j / 2] & 0xFFFFu) | 0x0C0C0000u;
-            sel_hi[j / 2] = (sel_hi[j / 2] & 0xFFFFu) | 0x0C0C0000u;
+            sel_lo[j / 2] = (sel_lo[j / 2] & ~kKeepJ1) | (0x0C0C0C0Cu & kKeepJ1);
+            sel_hi[j / 2] = (sel_hi[j / 2] & ~kKeepJ1) | (0x0C0C0C0Cu & kKeepJ1);
           }
         }
       }
@@ -497,16 +524,33 @@ void decode_kernel(DecodeParams p) {
         l = dot2_acc<dt>(pk, kOnes2<dt>, l);
         pg[0] = __uint_as_float(pk);
         all_gather<G>(pg);
+        if constexpr (F8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t v0 = vb[j][i], v1 = vb[j + 1][i];
-          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, sel_lo[j / 2]);   // column 2i of both tokens
-          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, sel_hi[j / 2]);   // column 2i+1
+          for (int i = 0; i < 2; ++i) {        // dword i: columns 4i .. 4i+3
+            const uint32_t v0 = vb[j][i], v1 = vb[j + 1][i];
+            const uint32_t lo = __builtin_amdgcn_perm(v1, v0, sel_lo[j / 2]);
+            const uint32_t hi = __builtin_amdgcn_perm(v1, v0, sel_hi[j / 2]);
+            const uint32_t col[4] = {widen_fp8_pair<dt, false>(lo), widen_fp8_pair<dt, true>(lo),
+                                     widen_fp8_pair<dt, false>(hi), widen_fp8_pair<dt, true>(hi)};
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t ph = __float_as_uint(pg[h]);
-            acc[h][2 * i] = dot2_acc<dt>(ph, lo, acc[h][2 * i]);
-            acc[h][2 * i + 1] = dot2_acc<dt>(ph, hi, acc[h][2 * i + 1]);
+            for (int h = 0; h < G; ++h) {
+              const uint32_t ph = __float_as_uint(pg[h]);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) acc[h][4 * i + k] = dot2_acc<dt>(ph, col[k], acc[h][4 * i + k]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t v0 = vb[j][i], v1 = vb[j + 1][i];
+            const uint32_t lo = __builtin_amdgcn_perm(v1, v0, sel_lo[j / 2]);   // column 2i of both tokens
+            const uint32_t hi = __builtin_amdgcn_perm(v1, v0, sel_hi[j / 2]);   // column 2i+1
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const uint32_t ph = __float_as_uint(pg[h]);
+              acc[h][2 * i] = dot2_acc<dt>(ph, lo, acc[h][2 * i]);
+              acc[h][2 * i + 1] = dot2_acc<dt>(ph, hi, acc[h][2 * i + 1]);
+            }
           }
         }
       }
@@ -521,7 +565,7 @@ void decode_kernel(DecodeParams p) {
   // back to the loop head has issued the refills in the same order as the
   // prologue and the compiler's load counters wait only for the buffer about
   // to be used.
-  u32x4 kbuf[NB][TPL], vbuf[NB][TPL];
+  KR kbuf[NB][TPL], vbuf[NB][TPL];
   bool okb[NB];
   const int first = SPLIT ? lo : lo + wave;
   if (first < hi) {
@@ -565,6 +609,13 @@ void decode_kernel(DecodeParams p) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+  }
+  if constexpr (F8) {
+    const float vs = p.v_scale[g];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= vs;
   }
   if constexpr (SPLIT) {                    // the wave's partial goes straight to the workspace
     if (r == 0) {
@@ -679,8 +730,13 @@ void splitkv_merge_kernel(DecodeParams p) {
 #ifndef PA_DECODE_NB_LARGEG
 #define PA_DECODE_NB_LARGEG 2
 #endif
-constexpr int decode_buffers(DT dt, int D, int G) {
-  return (dt == DT::F32 && D == 128) ? 2 : (G >= 4 ? PA_DECODE_NB_LARGEG : PA_DECODE_NB_SMALLG);
+#ifndef PA_DECODE_NB_FP8
+#define PA_DECODE_NB_FP8 4
+#endif
+constexpr int decode_buffers(DT dt, DT kt, int D, int G) {
+  // an fp8 buffer holds half the bytes of a 16-bit one
+  return kt == DT::FP8 ? PA_DECODE_NB_FP8
+                       : (dt == DT::F32 && D == 128) ? 2 : (G >= 4 ? PA_DECODE_NB_LARGEG : PA_DECODE_NB_SMALLG);
 }
 
 // Waves per workgroup; fp32 with head_dim 128 holds twice the bytes per lane
@@ -690,7 +746,7 @@ constexpr int decode_waves() {
   return (dt == DT::F32 && D == 128) ? 4 : (SPLIT ? PA_SPLITKV_WAVES : PA_DECODE_WAVES);
 }
 
-template <DT dt, int D, bool SPLIT>
+template <DT dt, DT kt, int D, bool SPLIT>
 static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   constexpr int W = decode_waves<dt, D, SPLIT>();
   const int G = p.num_q_heads / p.num_kv_heads;
@@ -704,10 +760,10 @@ static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   }
   dim3 block(64 * W);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<dt, D, 1, W, SPLIT, decode_buffers(dt, D, 1)>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<dt, D, 2, W, SPLIT, decode_buffers(dt, D, 2)>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<dt, D, 4, W, SPLIT, decode_buffers(dt, D, 4)>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<dt, D, 8, W, SPLIT, decode_buffers(dt, D, 8)>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 1, W, SPLIT, decode_buffers(dt, kt, D, 1)>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 2, W, SPLIT, decode_buffers(dt, kt, D, 2)>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 4, W, SPLIT, decode_buffers(dt, kt, D, 4)>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 8, W, SPLIT, decode_buffers(dt, kt, D, 8)>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -719,14 +775,25 @@ static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
 template <bool SPLIT>
 static hipError_t launch_any(const DecodeParams& p, hipStream_t s) {
   const DT dt = static_cast<DT>(p.dtype);
+  if (static_cast<DT>(p.kv_dtype) == DT::FP8) {
+    if (p.head_dim == 128) {
+      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 128, SPLIT>(p, s);
+      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 128, SPLIT>(p, s);
+    } else if (p.head_dim == 64) {
+      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 64, SPLIT>(p, s);
+      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 64, SPLIT>(p, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (p.kv_dtype != p.dtype) return hipErrorInvalidValue;
   if (p.head_dim == 128) {
-    if (dt == DT::F32) return launch_g<DT::F32, 128, SPLIT>(p, s);
-    if (dt == DT::F16) return launch_g<DT::F16, 128, SPLIT>(p, s);
-    if (dt == DT::BF16) return launch_g<DT::BF16, 128, SPLIT>(p, s);
+    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 128, SPLIT>(p, s);
+    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 128, SPLIT>(p, s);
+    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 128, SPLIT>(p, s);
   } else if (p.head_dim == 64) {
-    if (dt == DT::F32) return launch_g<DT::F32, 64, SPLIT>(p, s);
-    if (dt == DT::F16) return launch_g<DT::F16, 64, SPLIT>(p, s);
-    if (dt == DT::BF16) return launch_g<DT::BF16, 64, SPLIT>(p, s);
+    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 64, SPLIT>(p, s);
+    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 64, SPLIT>(p, s);
+    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 64, SPLIT>(p, s);
   }
   return hipErrorInvalidValue;
 }

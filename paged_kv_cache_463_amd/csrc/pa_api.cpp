@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 200;  // 0.2.0
+constexpr int32_t kVersion = 300;  // 0.3.0
 
 int elem_bytes(int32_t dtype) {
   switch (dtype) {
@@ -48,13 +48,14 @@ const void* device_view(const void* p) {
 }
 void* device_view(void* p) { return const_cast<void*>(device_view(static_cast<const void*>(p))); }
 
-// Checks shared by the attention entry points.
+// Checks shared by the attention entry points. `cache_bytes` is the cache's
+// element size when it differs from the query type (1 for an FP8 cache).
 int32_t check_attention_common(const void* out, const void* query, const void* k_cache,
                                const void* v_cache, int64_t block_stride, int64_t num_blocks,
                                const int32_t* block_tables, int32_t block_table_stride,
                                const int32_t* lens, int32_t num_seqs, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t dtype) {
+                               int32_t dtype, int cache_bytes = 0) {
   if (elem_bytes(dtype) == 0) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
       block_table_stride < 0)
@@ -67,12 +68,14 @@ int32_t check_attention_common(const void* out, const void* query, const void* k
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !lens) return PA_ERR_NULL_PTR;
   if (num_blocks == 0 || block_table_stride == 0) return PA_ERR_SHAPE;
-  const int e = elem_bytes(dtype);
+  const int e = cache_bytes ? cache_bytes : elem_bytes(dtype);
   if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (block_stride * e) % 16 != 0)
     return PA_ERR_ALIGNMENT;
   return PA_OK;
 }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 pa::DecodeParams make_decode_params(void* out, const void* query, const void* k_cache,
                                     const void* v_cache, int64_t block_stride, int64_t num_blocks,
@@ -95,11 +98,31 @@ pa::DecodeParams make_decode_params(void* out, const void* query, const void* k_
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.dtype = dtype;
+  p.kv_dtype = dtype;
   p.scale = scale;
   return p;
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Turns a decode parameter block into its FP8-cache form.
+void make_fp8(pa::DecodeParams& p, int64_t block_stride, const float* k_scale, const float* v_scale) {
+  p.kv_dtype = pa::kKvFp8;
+  p.block_stride_bytes = block_stride;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+}
+
+// Split-KV workspace carving: fp32 partial outputs, (max, normaliser) pairs,
+// the work counter; each part 256-byte aligned.
+void carve_splitkv(pa::DecodeParams& p, void* workspace, int32_t mcl, int32_t partition_size) {
+  p.partition_blocks = partition_size / 16;
+  p.max_parts = (int32_t)ceil_div(mcl, partition_size);
+  const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads * p.max_parts;
+  p.ws_acc = static_cast<float*>(workspace);
+  const int64_t acc_bytes = ceil_div(rows * p.head_dim * 4, 256) * 256;
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes);
+  p.ws_ctr = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + acc_bytes +
+                                        ceil_div(rows * 2 * 4, 256) * 256);
+}
 
 }  // namespace
 
@@ -275,14 +298,94 @@ int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, con
                                           block_tables, block_table_stride, context_lens,
                                           num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
                                           dtype);
-  p.partition_blocks = partition_size / 16;
-  p.max_parts = (int32_t)ceil_div(mcl, partition_size);
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * p.max_parts;
-  p.ws_acc = static_cast<float*>(workspace);
-  const int64_t acc_bytes = ceil_div(rows * head_dim * 4, 256) * 256;
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes);
-  p.ws_ctr = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + acc_bytes +
-                                        ceil_div(rows * 2 * 4, 256) * 256);
+  carve_splitkv(p, workspace, mcl, partition_size);
+  return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                                 void* k_cache, void* v_cache, int64_t block_stride,
+                                 int64_t num_blocks, const int32_t* slot_mapping, int64_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 const float* k_scale, const float* v_scale, int32_t dtype,
+                                 void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (kv_token_stride < row || block_stride < block_size * row) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+    return PA_ERR_NULL_PTR;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (kv_token_stride * e) % 16 != 0 || block_stride % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::ScatterParams p{};
+  p.key = key;
+  p.value = value;
+  p.token_stride_bytes = kv_token_stride * e;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride;
+  p.num_slots = num_blocks * block_size;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.row_bytes = (int32_t)row;
+  p.in_dtype = dtype;
+  p.head_dim = head_dim;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  return hip_status(pa::launch_reshape_and_cache_fp8(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                      int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                      int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, const float* k_scale, const float* v_scale,
+                      int32_t dtype, void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype, 1);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!k_scale || !v_scale) return PA_ERR_NULL_PTR;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  make_fp8(p, block_stride, k_scale, v_scale);
+  return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_splitkv_fp8(void* out, const void* query, const void* k_cache,
+                              const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float scale, const float* k_scale, const float* v_scale,
+                              int32_t dtype, int32_t max_context_len, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype, 1);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_scale || !v_scale) return PA_ERR_NULL_PTR;
+  const int32_t mcl = max_context_len > 0 ? max_context_len : 1;
+  const size_t need = pa_decode_splitkv_workspace_bytes(num_seqs, num_q_heads, head_dim, mcl,
+                                                        partition_size);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  make_fp8(p, block_stride, k_scale, v_scale);
+  carve_splitkv(p, workspace, mcl, partition_size);
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 

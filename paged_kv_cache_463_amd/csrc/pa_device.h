@@ -7,11 +7,14 @@
 
 namespace pa {
 
-enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+// F32, F16 and BF16 name both query/output and cache types; FP8 (OCP e4m3)
+// names a cache type only.
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 constexpr int kBlockSize = 16;   // tokens per physical block
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -20,6 +23,7 @@ template <DT dt> struct Elem;
 template <> struct Elem<DT::F32>  { static constexpr int bytes = 4; };
 template <> struct Elem<DT::F16>  { static constexpr int bytes = 2; };
 template <> struct Elem<DT::BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT::FP8>  { static constexpr int bytes = 1; };
 
 // ---------------------------------------------------------------------------
 // DPP lane exchanges inside a row of 16 lanes.
@@ -133,6 +137,48 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 e4m3 (OCP 8-bit floating point E4M3: bias 7, 3 mantissa bits,
+// subnormals, no infinities, NaN = S.1111.111, largest finite 448)
+// ---------------------------------------------------------------------------
+// Nearest code of a float, ties to the even mantissa; finite values past
+// +-448 and infinities saturate to +-448; NaN stays NaN; the sign of zero is
+// kept. Below 2^-6 the codes are the subnormal steps of 2^-9, so the code is
+// |y| * 2^9 rounded to an integer (8 is the smallest normal); above it the
+// float's mantissa is rounded to 3 bits in place and the exponent rebased.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;                 // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;                // >= 448 (inf included)
+  if (a < 0x3C800000u)                                      // < 2^-6
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);       // round 23 -> 3 mantissa bits
+  return sign | (((r >> 20) - (120u << 3)) & 0x7Fu);        // exponent bias 127 -> 7
+}
+
+// Four e4m3 codes of one dword -> two dwords of packed 16-bit values (the
+// query type), byte pairs (0,1) and (2,3). Every e4m3 value is exact in f16
+// and bf16; the conversion scale is 1.
+template <DT dt, bool HI>
+__device__ __forceinline__ uint32_t widen_fp8_pair(uint32_t w) {
+  if constexpr (dt == DT::BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+template <DT dt>
+__device__ __forceinline__ u32x4 widen_fp8(const u32x2& w) {
+  const uint32_t w0 = w[0], w1 = w[1];
+  return u32x4{widen_fp8_pair<dt, false>(w0), widen_fp8_pair<dt, true>(w0),
+               widen_fp8_pair<dt, false>(w1), widen_fp8_pair<dt, true>(w1)};
 }
 
 }  // namespace pa

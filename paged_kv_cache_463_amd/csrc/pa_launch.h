@@ -8,6 +8,8 @@
 
 namespace pa {
 
+constexpr int32_t kKvFp8 = 3;   // DecodeParams::kv_dtype of an FP8 (e4m3) cache
+
 struct ScatterParams {
   const void* key;
   const void* value;
@@ -18,7 +20,12 @@ struct ScatterParams {
   int64_t num_slots;            // num_blocks * block_size
   const int32_t* slot_mapping;
   int64_t num_tokens;
-  int32_t row_bytes;            // num_kv_heads * head_dim * element bytes
+  int32_t row_bytes;            // num_kv_heads * head_dim * cache element bytes
+  // FP8 (e4m3) cache only: input element type, head_dim, per-kv-head scales
+  int32_t in_dtype;
+  int32_t head_dim;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct DecodeParams {
@@ -35,7 +42,10 @@ struct DecodeParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t dtype;
+  int32_t dtype;                // query / output type
+  int32_t kv_dtype;             // cache type: dtype, or FP8 (e4m3)
+  const float* k_scale;         // FP8 cache: [num_kv_heads] dequantisation scales
+  const float* v_scale;
   float scale;
   // split-KV only
   int32_t partition_blocks;     // partition_size / 16
@@ -78,6 +88,7 @@ struct BlockCopyParams {
 };
 
 hipError_t launch_reshape_and_cache(const ScatterParams& p, hipStream_t s);
+hipError_t launch_reshape_and_cache_fp8(const ScatterParams& p, hipStream_t s);
 constexpr int kSwapChunk = 240;              // pairs per swap launch (kernel-argument space)
 struct SwapChunk {
   void* dst;                    // both pools addressable by the device

@@ -117,6 +117,53 @@ def test_prefill_checks():
     assert call(B=0) == OK
 
 
+def _scatter_fp8(**kw):
+    a = dict(key=FAKE, value=FAKE, ts=8 * 128, k=FAKE, v=FAKE, bstride=16 * 8 * 128, nb=10, slots=FAKE,
+             T=5, hkv=8, d=128, bs=16, ks=FAKE, vs=FAKE, dtype=2)
+    a.update(kw)
+    return P.lib().pa_reshape_and_cache_fp8(a["key"], a["value"], a["ts"], a["k"], a["v"], a["bstride"],
+                                            a["nb"], a["slots"], a["T"], a["hkv"], a["d"], a["bs"],
+                                            a["ks"], a["vs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), NULL), (dict(vs=None), NULL), (dict(key=None), NULL), (dict(dtype=3), DTYPE),
+    (dict(d=96), UNSUP), (dict(bstride=16 * 8 * 128 - 16), SHAPE), (dict(bstride=16 * 8 * 128 + 8), ALIGN),
+    (dict(ts=8 * 128 + 4), ALIGN), (dict(dtype=0, ts=8 * 128 + 2), ALIGN), (dict(T=0, ks=None), OK),
+])
+def test_scatter_fp8_argument_checks(kw, code):
+    assert _scatter_fp8(**kw) == code
+
+
+def _decode_fp8(split=False, **kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, block_stride=16 * 4 * 128, num_blocks=32, bt=FAKE,
+             bt_stride=3, lens=FAKE, B=4, hq=8, hkv=4, d=128, bs=16, scale=0.088, ks=FAKE, vs=FAKE, dtype=2,
+             mcl=48, part=512, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    args = [a["out"], a["query"], a["k"], a["v"], a["block_stride"], a["num_blocks"], a["bt"], a["bt_stride"],
+            a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"], a["ks"], a["vs"], a["dtype"]]
+    if split:
+        return P.lib().pa_decode_splitkv_fp8(*args, a["mcl"], a["part"], a["ws"], a["wsb"], None)
+    return P.lib().pa_decode_fp8(*args, None)
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), DTYPE), (dict(dtype=3), DTYPE), (dict(ks=None), NULL), (dict(vs=None), NULL),
+    (dict(out=None), NULL), (dict(d=96), UNSUP), (dict(hq=64, hkv=4), UNSUP),
+    (dict(block_stride=16 * 4 * 128 - 16), SHAPE), (dict(block_stride=16 * 4 * 128 + 8), ALIGN),
+    (dict(k=MIS), ALIGN), (dict(B=0), OK), (dict(B=0, ks=None), OK),
+])
+def test_decode_fp8_argument_checks(split, kw, code):
+    assert _decode_fp8(split, **kw) == code
+
+
+def test_splitkv_fp8_workspace_checks():
+    assert _decode_fp8(True, wsb=16) == WS
+    assert _decode_fp8(True, ws=None) == WS
+    assert _decode_fp8(True, part=100) == SHAPE
+
+
 def test_binding_raises_on_error_status():
     err = P.PagedAttentionError("pa_decode", 4)
     assert "PA_ERR_UNSUPPORTED" in str(err) and err.status == 4

@@ -288,6 +288,38 @@ def make_decode(name: str, dtype: str, context_lens, num_q_heads: int, num_kv_he
 
 
 # ----------------------------------------------------------------------------
+# FP8 (e4m3) cache contents for a decode case
+# ----------------------------------------------------------------------------
+E4M3_NAN_CODES = (0x7F, 0xFF)     # S.1111.111 in the OCP E4M3 format
+
+
+@dataclass
+class Fp8Pools:
+    k_pool: np.ndarray                # uint8 codes [num_blocks, 16, H_kv, D]
+    v_pool: np.ndarray
+    k_scale: np.ndarray               # float32 [H_kv]
+    v_scale: np.ndarray
+
+
+def fp8_pools(case: DecodeCase, seed: int = 0) -> Fp8Pools:
+    """Cache contents of ``case`` as e4m3 codes: every live slot holds codes drawn
+    uniformly from the 254 non-NaN codes (magnitudes spread over the whole format,
+    subnormals included); every slot the 16-bit pools poison (free blocks, tails,
+    the new tokens' slots) holds a NaN code. Per-kv-head scales are drawn from
+    [1/448, 1/112], so stored values reach +-1 to +-4."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 8]))
+    finite = np.array([c for c in range(256) if c not in E4M3_NAN_CODES], dtype=np.uint8)
+    out = []
+    for pool in (case.k_pool, case.v_pool):
+        codes = finite[rng.integers(0, len(finite), size=pool.shape, dtype=np.uint8)]
+        codes[is_nan_storage(pool, case.dtype)] = E4M3_NAN_CODES[0]
+        out.append(codes)
+    ks = rng.uniform(1 / 448, 1 / 112, case.num_kv_heads).astype(np.float32)
+    vs = rng.uniform(1 / 448, 1 / 112, case.num_kv_heads).astype(np.float32)
+    return Fp8Pools(out[0], out[1], ks, vs)
+
+
+# ----------------------------------------------------------------------------
 # prefill cases
 # ----------------------------------------------------------------------------
 @dataclass
