@@ -16,6 +16,9 @@ the pages it cites:
   ``ceil(L / block_size)`` logical blocks, take K and V rows from the physical
   blocks, score ``q·k / sqrt(d)``, softmax, and weight V (page
   "vLLM推理引擎深度解析" §五, ``PagedAttention.forward``);
+* ``append_slot`` + ``paged_decode_step``: a whole decode step, the new token
+  written at position ``L - 1`` through the table, then decode (the same
+  pages' append rule and forward);
 * ``decode_partials`` + ``lse_merge``: the same softmax split over token
   partitions and recombined by log-sum-exp (not on the pages; the identity is
   exact in exact arithmetic, so the merged result must equal ``paged_decode``);
@@ -53,6 +56,8 @@ from .paged_attention import (  # noqa: F401
     gather,
     attend,
     paged_decode,
+    append_slot,
+    paged_decode_step,
     decode_partials,
     lse_merge,
     paged_decode_splitkv,

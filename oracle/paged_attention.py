@@ -118,6 +118,30 @@ def paged_decode(query, k_pool, v_pool, block_tables, context_lens, scale, num_k
     return out
 
 
+def append_slot(table_row: np.ndarray, length: int, block_size: int = BLOCK_SIZE) -> int:
+    """Slot of the newest token of a sequence holding ``length`` tokens: position
+    ``length - 1`` sits in row ``(length-1) % block_size`` of the physical block that
+    table entry ``(length-1) // block_size`` names (the append of page
+    "vLLM推理引擎深度解析" §三: the last block while it has room, else a fresh block the
+    manager has put at the end of the table). ``length == 0``: no token, -1."""
+    if length <= 0:
+        return -1
+    pos = length - 1
+    return int(table_row[pos // block_size]) * block_size + pos % block_size
+
+
+def paged_decode_step(query, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, num_kv_heads,
+                      dtype, block_size: int = BLOCK_SIZE):
+    """One decode step: each sequence's new K/V row is written at its newest position
+    (``append_slot``), then every sequence attends over its ``L_b`` cached tokens.
+    Returns ``(out, k_pool', v_pool')``."""
+    slots = np.array([append_slot(block_tables[b], int(context_lens[b]), block_size)
+                      for b in range(len(context_lens))], dtype=np.int64)
+    kp, vp = scatter(k_pool, v_pool, k_new, v_new, slots, block_size)
+    out = paged_decode(query, kp, vp, block_tables, context_lens, scale, num_kv_heads, dtype, block_size)
+    return out, kp, vp
+
+
 # ----------------------------------------------------------------------------
 # split-KV: partition partials and their log-sum-exp merge
 # ----------------------------------------------------------------------------

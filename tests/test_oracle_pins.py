@@ -152,6 +152,39 @@ def test_scatter_matches_flat_slot_write(dtype):
     assert ok.reshape(nb * 16, H, D)[untouched].tobytes() == kp.reshape(nb * 16, H, D)[untouched].tobytes()
 
 
+def test_append_slot_matches_golden_positions():
+    g = json.load(open(GOLDEN))
+    bs = g["block_size"]
+    for c in g["new_token_position"]["cases"]:
+        n = c["cached_before"]                                 # the new token makes it n + 1
+        row = np.arange(1000, 1000 + n // bs + 1)
+        slot = oracle.append_slot(row, n + 1)
+        assert (slot // bs - 1000, slot % bs) == (c["logical_block"], c["offset"])
+    assert oracle.append_slot(np.array([5]), 0) == -1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_step_equals_scatter_then_decode(dtype):
+    """The step writes each new token where the harness's append rule put it (the slots are
+    derived independently, from the case's own slot_mapping) and then decodes."""
+    c = _small_decode(dtype, lens=(0, 1, 15, 16, 17, 33, 64))
+    out, kp, vp = oracle.paged_decode_step(c.query, c.k_new, c.v_new, c.k_pool, c.v_pool, c.block_tables,
+                                           c.context_lens, c.scale, c.num_kv_heads, dtype)
+    rk, rv = oracle.scatter(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+    assert kp.tobytes() == rk.tobytes() and vp.tobytes() == rv.tobytes()
+    ref = oracle.paged_decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, c.num_kv_heads, dtype)
+    assert np.array_equal(out, ref)
+    assert np.all(out[0] == 0)                                 # empty sequence: zeros, nothing written
+
+
+def test_mutation_append_slot_off_by_one_is_caught(monkeypatch):
+    def bad(table_row, length, block_size=16):
+        return -1 if length <= 0 else int(table_row[length // block_size]) * block_size + length % block_size
+    monkeypatch.setattr(OPA, "append_slot", bad)
+    with pytest.raises((AssertionError, IndexError)):
+        test_decode_step_equals_scatter_then_decode("f32")
+
+
 def test_scatter_then_gather_returns_new_token():
     c = _small_decode("bf16")
     kp, vp = _scattered(c)
