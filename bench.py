@@ -143,7 +143,7 @@ def stored_traffic(workload: str, call: str, partition: int):
 # device state and one step
 # ----------------------------------------------------------------------------
 class Runner:
-    def __init__(self, case, call: str, layers: int, partition: int):
+    def __init__(self, case, call: str, layers: int, partition: int, step_mode: str = "separate"):
         import torch
         import paged_kv_cache_463_amd as P
         import workloads as W
@@ -185,6 +185,39 @@ class Runner:
             need = P.splitkv_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, self.mcl, partition)
             self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         assert self.q.dtype == dt
+        self.step_mode = step_mode
+        self.graph = None
+        if step_mode == "graph":                   # one recording of the fused step of every layer
+            self.graph = P.StepGraph()
+            with self.graph:
+                for layer in range(layers):
+                    self.fused(layer, stream=self.graph.stream)
+
+    def fused(self, layer: int, stream=None):
+        c, P = self.case, self.P
+        if self.fp8:
+            P.decode_step_fp8(self.out, self.q, self.kn, self.vn, self.kp[layer], self.vp[layer], self.bt,
+                              self.lens, c.scale, self.ks, self.vs, stream=stream)
+        else:
+            P.decode_step(self.out, self.q, self.kn, self.vn, self.kp[layer], self.vp[layer], self.bt, self.lens,
+                          c.scale, stream=stream)
+
+    def step(self, layer: int, ev=None):
+        """One step (graph mode: one replay = the steps of all layers); ``ev`` = (start, end)
+        events recorded around the attention launch (the replay)."""
+        stream = self.torch.cuda.current_stream()
+        if self.step_mode == "separate":
+            self.scatter(layer)
+        if ev:
+            ev[0].record(stream)
+        if self.step_mode == "separate":
+            self.attend(layer)
+        elif self.step_mode == "fused":
+            self.fused(layer)
+        else:
+            self.graph.replay()
+        if ev:
+            ev[1].record(stream)
 
     def scatter(self, layer: int):
         if self.fp8:
@@ -215,22 +248,18 @@ def time_steps(r: Runner, steps: int, warmup: int):
     """Warm up, then time exactly ``steps`` steps; HIP events bracket every attention
     call on the launch stream."""
     torch = r.torch
-    for i in range(warmup):
-        r.scatter(i % r.layers)
-        r.attend(i % r.layers)
+    per = r.layers if r.step_mode == "graph" else 1      # steps covered by one call of r.step
+    for i in range(0, warmup, per):
+        r.step(i % r.layers)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    n = steps // per
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     t0 = time.perf_counter()
-    for i in range(steps):
-        layer = i % r.layers
-        r.scatter(layer)
-        ev[i][0].record(stream)
-        r.attend(layer)
-        ev[i][1].record(stream)
+    for i in range(n):
+        r.step((i * per) % r.layers, ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_ms = [a.elapsed_time(b) / per for a, b in ev]
     return elapsed, attn_ms
 
 
@@ -291,6 +320,20 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
 
 
 # ----------------------------------------------------------------------------
+def calibration_copy(mib: int) -> None:
+    """A plain device-to-device copy of ``mib`` MiB, three times (HBM counter calibration);
+    issued right before the timed steps, after every other copy of the set-up."""
+    if not mib:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_block_copy(args) -> int:
     """pa_copy_blocks over a batch of copy-on-write pairs (one launch = one step), plus the
     device <-> pinned-host swap rates of pa_swap_blocks (copy engine, host-link bound)."""
@@ -308,6 +351,7 @@ def bench_block_copy(args) -> int:
     pairs = torch.from_numpy(pairs_np).cuda()
     block_bytes = 16 * hkv * d * 2
     alg = npairs * 2 * block_bytes * 2                  # K and V, read and write
+    calibration_copy(args.copy_calibration_mib)
     for i in range(args.warmup):
         P.copy_blocks(kp[i % args.layers], vp[i % args.layers], pairs)
     torch.cuda.synchronize()
@@ -379,6 +423,9 @@ def main(argv=None) -> int:
     ap.add_argument("--layers", type=int, default=4, help="KV pool replicas rotated over steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-mode", default="separate", choices=["separate", "fused", "graph"],
+                    help="separate: scatter launch + attention launch; fused: one pa_decode_step launch; "
+                         "graph: the fused step replayed from a HIP graph (single-pass decode only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -398,17 +445,16 @@ def main(argv=None) -> int:
     t_gen = time.perf_counter()
     case = W.NAMED[gen_key]()
     t_gen = time.perf_counter() - t_gen
-    r = Runner(case, call, args.layers, args.partition)
+    if args.step_mode != "separate" and call not in ("decode", "decode_fp8"):
+        print("--step-mode fused/graph applies to the single-pass decode workloads", file=sys.stderr)
+        return 2
+    if args.step_mode == "graph" and args.steps % args.layers:
+        print("--step-mode graph replays all layers at once: --steps must be a multiple of --layers",
+              file=sys.stderr)
+        return 2
+    r = Runner(case, call, args.layers, args.partition, args.step_mode)
     print(f"# workload {args.workload}: generated in {t_gen:.1f} s, kernel {call}", file=sys.stderr, flush=True)
-
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args.copy_calibration_mib)
 
     elapsed, attn_ms = time_steps(r, args.steps, args.warmup)
     attn_us = float(np.mean(attn_ms)) * 1e3
@@ -417,7 +463,8 @@ def main(argv=None) -> int:
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": case.dtype, "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)"}
-    cfg = {"workload": args.workload, "kernel": call, "block_size": 16, "num_seqs": case.num_seqs,
+    cfg = {"workload": args.workload, "kernel": call, "step_mode": args.step_mode, "block_size": 16,
+           "num_seqs": case.num_seqs,
            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
            "kv_pool_replicas": args.layers}
     if call == "prefill":

@@ -22,7 +22,9 @@
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
  *     `stream`, which is a hipStream_t passed as void* (NULL = null stream).
  *     The library allocates nothing, frees nothing, keeps no pointer after it
- *     returns and has no mutable global state; calls are thread-safe.
+ *     returns and has no mutable global state; calls are thread-safe. The
+ *     exceptions are the handle objects: a block manager (pa_bm_*) and a
+ *     step graph (pa_graph_*) own their memory until destroyed.
  *   - Every call only enqueues work on `stream` and returns; stream order is
  *     what makes a cache write visible to a later attention call.
  *   - `dtype` is a pa_dtype_t. Element types: F32 = float, F16 = IEEE half,
@@ -167,6 +169,52 @@ PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cac
                           size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_step — one whole decode step in one launch: each sequence's new
+ * token (key_new/value_new row b) is written at position L_b - 1 of its cache,
+ * in the slot its block table names (row (L_b-1) % 16 of physical block
+ * block_tables[b][(L_b-1) / 16], the append rule of [P1] §三), then every
+ * sequence attends over its L_b cached tokens exactly as pa_decode does. The
+ * result equals pa_reshape_and_cache with those slots followed by pa_decode;
+ * no slot_mapping is needed, and a sequence with L_b == 0 writes nothing.
+ *
+ *   key_new, value_new  [num_seqs][num_kv_heads][head_dim] of dtype, row b at
+ *                       element b * kv_token_stride (>= H_kv*D)
+ *   k_cache, v_cache    written (the new rows) and read
+ * Other arguments and errors as pa_decode. The workgroup of (sequence,
+ * kv head) writes its own head's new row before reading the cache; the
+ * table entry of position L_b - 1 must name a block no other sequence reads
+ * (a shared block is copied first, see pa_copy_blocks).
+ */
+PA_API int32_t pa_decode_step(void* out, const void* query, const void* key_new, const void* value_new,
+                       int64_t kv_token_stride, void* k_cache, void* v_cache, int64_t block_stride,
+                       int64_t num_blocks, const int32_t* block_tables, int32_t block_table_stride,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                       int32_t dtype, void* stream);
+
+/*
+ * Step graphs ([P3] §5.3 captures the decode step per batch size as a CUDA
+ * graph; here a HIP graph). pa_graph_begin creates a capture stream (a
+ * non-blocking stream of default priority) and starts recording it; library
+ * calls issued on *capture_stream are recorded, not run, until pa_graph_end
+ * instantiates them. pa_graph_launch replays the recording on `stream`.
+ * Pointers, sizes and grids are frozen at capture; device memory (lengths,
+ * tables, K/V, queries) is read at replay, so one graph serves every step of
+ * a batch size whose buffers keep their addresses. Recordable calls: those
+ * that only launch kernels (every call except pa_swap_blocks and the pa_bm_*
+ * host calls). The graph owns its stream and executable until
+ * pa_graph_destroy (which also abandons an unfinished recording). A graph is
+ * not thread-safe; replays on one stream are ordered like any launch.
+ * Errors: PA_ERR_NULL_PTR, PA_ERR_SHAPE (end without begin, launch before
+ * end), PA_ERR_HIP (the runtime refused to capture or instantiate).
+ */
+typedef struct pa_graph pa_graph;
+PA_API int32_t pa_graph_begin(pa_graph** graph, void** capture_stream);
+PA_API int32_t pa_graph_end(pa_graph* graph);
+PA_API int32_t pa_graph_launch(pa_graph* graph, void* stream);
+PA_API void pa_graph_destroy(pa_graph* graph);
+
+/*
  * FP8 KV cache. [P3] (introduction) lists FP8 among the quantisation schemes
  * the engine supports and gives no format; the format here is the OCP 8-bit
  * floating point E4M3 ("e4m3fn": bias 7, 3 mantissa bits, subnormals, no
@@ -226,6 +274,20 @@ PA_API int32_t pa_decode_splitkv_fp8(void* out, const void* query, const void* k
                               float scale, const float* k_scale, const float* v_scale,
                               int32_t dtype, int32_t max_context_len, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_step_fp8 — pa_decode_step over an FP8 cache: the new rows (of
+ * dtype, the query type) are quantised as in pa_reshape_and_cache_fp8, then
+ * decode as pa_decode_fp8. block_stride is in bytes.
+ */
+PA_API int32_t pa_decode_step_fp8(void* out, const void* query, const void* key_new, const void* value_new,
+                           int64_t kv_token_stride, void* k_cache, void* v_cache,
+                           int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                           int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, float scale,
+                           const float* k_scale, const float* v_scale, int32_t dtype,
+                           void* stream);
 
 /*
  * pa_copy_blocks — the device half of copy-on-write ([P2] Block 管理器: requests

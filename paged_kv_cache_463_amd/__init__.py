@@ -12,8 +12,11 @@ from ._binding import (  # noqa: F401
     swap_blocks,
     LibraryNotBuilt,
     PagedAttentionError,
+    StepGraph,
     decode,
     decode_fp8,
+    decode_step,
+    decode_step_fp8,
     decode_splitkv,
     decode_splitkv_fp8,
     lib,
@@ -24,6 +27,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
-           "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8",
+           "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8", "decode_step", "decode_step_fp8",
+           "StepGraph",
            "prefill_chunked", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
            "LibraryNotBuilt", "PagedAttentionError"]

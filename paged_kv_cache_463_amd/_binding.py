@@ -37,6 +37,14 @@ SIGNATURES = {
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
+    "pa_decode_step": (_i32, [_p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _i32, _p]),
+    "pa_decode_step_fp8": (_i32, [_p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32,
+                                   _i32, _i32, _f32, _p, _p, _i32, _p]),
+    "pa_graph_begin": (_i32, [_p, _p]),
+    "pa_graph_end": (_i32, [_p]),
+    "pa_graph_launch": (_i32, [_p, _p]),
+    "pa_graph_destroy": (None, [_p]),
     "pa_reshape_and_cache_fp8": (_i32, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _i32, _i32, _i32, _p, _p,
                                          _i32, _p]),
     "pa_decode_fp8": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32,
@@ -181,6 +189,90 @@ def decode_splitkv(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
         max_context_len, partition_size, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def _step_rows(key_new: torch.Tensor, value_new: torch.Tensor, B: int, hkv: int, d: int):
+    _require(key_new.shape == value_new.shape and key_new.stride() == value_new.stride(), "key_new/value_new differ")
+    _require(key_new.dim() == 3 and key_new.shape[0] == B and key_new.shape[1] == hkv and key_new.shape[2] == d
+             and key_new.stride(2) == 1 and key_new.stride(1) == d, "new rows must be [B, H_kv, D], rows contiguous")
+
+
+def decode_step(out: torch.Tensor, query: torch.Tensor, key_new: torch.Tensor, value_new: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                context_lens: torch.Tensor, scale: float, stream=None) -> None:
+    """One decode step in one launch: row b of ``key_new``/``value_new`` goes to position
+    ``context_lens[b] - 1`` through the table, then the single-pass decode."""
+    nb, bs, hkv, d, bstride = _pool_dims(k_cache)
+    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
+    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(context_lens, "context_lens")
+    B, hq, _ = query.shape
+    _step_rows(key_new, value_new, B, hkv, d)
+    _check("pa_decode_step", lib().pa_decode_step(
+        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), key_new.stride(0), _ptr(k_cache), _ptr(v_cache),
+        bstride, nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale,
+        _dtype(query), _stream(stream)))
+
+
+def decode_step_fp8(out: torch.Tensor, query: torch.Tensor, key_new: torch.Tensor, value_new: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, scale: float, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                    stream=None) -> None:
+    """``decode_step`` over FP8 pools: the new rows are quantised on the way in."""
+    nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
+    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(context_lens, "context_lens")
+    B, hq, _ = query.shape
+    _step_rows(key_new, value_new, B, hkv, d)
+    _check("pa_decode_step_fp8", lib().pa_decode_step_fp8(
+        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), key_new.stride(0), _ptr(k_cache), _ptr(v_cache),
+        bstride, nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale,
+        _ptr(k_scale), _ptr(v_scale), _dtype(query), _stream(stream)))
+
+
+class StepGraph:
+    """A recorded sequence of library calls, replayed as one HIP graph launch.
+
+    ``with StepGraph() as g: decode_step(..., stream=g.stream)`` records the calls made on
+    ``g.stream`` (nothing runs while recording); ``g.replay()`` launches the recording on
+    the current stream. Tensor addresses and sizes are frozen at capture; contents are read
+    at every replay."""
+
+    def __init__(self):
+        self._h = ctypes.c_void_p()
+        self._s = ctypes.c_void_p()
+        self._ended = False
+
+    def __enter__(self):
+        _check("pa_graph_begin", lib().pa_graph_begin(ctypes.byref(self._h), ctypes.byref(self._s)))
+        return self
+
+    @property
+    def stream(self) -> int:
+        """The capture stream, as an integer handle accepted by the ``stream`` arguments."""
+        return self._s.value
+
+    def __exit__(self, exc_type, exc, tb):
+        if exc_type is None:
+            _check("pa_graph_end", lib().pa_graph_end(self._h))
+            self._ended = True
+        return False
+
+    def replay(self, stream=None) -> None:
+        _check("pa_graph_launch", lib().pa_graph_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if self._h.value:
+            lib().pa_graph_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _fp8_pools(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor):

@@ -360,6 +360,43 @@ void decode_kernel(DecodeParams p) {
   }
   const int hq0 = g * G;
 
+  // Fused decode step: the workgroup of (sequence b, kv head g) is the only one
+  // that reads head g of b's newest row, so it writes that row itself (the
+  // slot the table names for position L-1, as the append rule puts it) and a
+  // barrier, whose workgroup-scope fences order the stores before every
+  // wave's loads, separates the write from the attention.
+  if constexpr (!SPLIT) {
+    if (p.key_new) {                        // uniform: a kernel argument
+      const int pos = p.context_lens[b] - 1;
+      constexpr int NCH = D / 8;            // 8-element chunks of one head's row
+      if (pos >= 0 && pos / kBlockSize < p.block_table_stride && threadIdx.x < 2 * NCH) {
+        const int bid = p.block_tables[(int64_t)b * p.block_table_stride + pos / kBlockSize];
+        if (bid >= 0 && bid < p.num_blocks) {
+          const int kv = threadIdx.x / NCH, ch = threadIdx.x % NCH;
+          const char* src = static_cast<const char*>(kv ? p.value_new : p.key_new) +
+                            (int64_t)b * p.new_token_stride_bytes + ((int64_t)g * D + ch * 8) * E;
+          char* dst = static_cast<char*>(const_cast<void*>(kv ? p.v_cache : p.k_cache)) +
+                      (int64_t)bid * p.block_stride_bytes +
+                      (((int64_t)(pos % kBlockSize) * p.num_kv_heads + g) * D + ch * 8) * KE;
+          if constexpr (F8) {
+            float x[8];
+            unpack<dt>(load16(src), x);
+            const float sc = (kv ? p.v_scale : p.k_scale)[g];
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_encode(x[i] / sc) << (8 * (i & 3));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+          } else {
+#pragma unroll
+            for (int c16 = 0; c16 < E / 2; ++c16)   // 8 elements: one or two 16-byte chunks
+              *reinterpret_cast<u32x4*>(dst + 16 * c16) = load16(src + 16 * c16);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   // single pass: the W waves share the sequence's blocks round-robin.

@@ -302,6 +302,60 @@ int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, con
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_decode_step(void* out, const void* query, const void* key_new, const void* value_new,
+                       int64_t kv_token_stride, void* k_cache, void* v_cache, int64_t block_stride,
+                       int64_t num_blocks, const int32_t* block_tables, int32_t block_table_stride,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                       int32_t dtype, void* stream) {
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  const int e = elem_bytes(dtype);
+  if (!key_new || !value_new) return PA_ERR_NULL_PTR;
+  if (kv_token_stride < (int64_t)num_kv_heads * head_dim) return PA_ERR_SHAPE;
+  if (!aligned16(key_new) || !aligned16(value_new) || (kv_token_stride * e) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  p.key_new = key_new;
+  p.value_new = value_new;
+  p.new_token_stride_bytes = kv_token_stride * e;
+  return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_step_fp8(void* out, const void* query, const void* key_new, const void* value_new,
+                           int64_t kv_token_stride, void* k_cache, void* v_cache,
+                           int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                           int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, float scale,
+                           const float* k_scale, const float* v_scale, int32_t dtype,
+                           void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype, 1);
+  if (st != PA_OK || num_seqs == 0) return st;
+  const int e = elem_bytes(dtype);
+  if (!key_new || !value_new || !k_scale || !v_scale) return PA_ERR_NULL_PTR;
+  if (kv_token_stride < (int64_t)num_kv_heads * head_dim) return PA_ERR_SHAPE;
+  if (!aligned16(key_new) || !aligned16(value_new) || (kv_token_stride * e) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  make_fp8(p, block_stride, k_scale, v_scale);
+  p.key_new = key_new;
+  p.value_new = value_new;
+  p.new_token_stride_bytes = kv_token_stride * e;
+  return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t kv_token_stride,
                                  void* k_cache, void* v_cache, int64_t block_stride,
                                  int64_t num_blocks, const int32_t* slot_mapping, int64_t num_tokens,

@@ -47,6 +47,12 @@ struct DecodeParams {
   const float* k_scale;         // FP8 cache: [num_kv_heads] dequantisation scales
   const float* v_scale;
   float scale;
+  // fused decode step (single pass only): this step's token of each sequence,
+  // [num_seqs][num_kv_heads][head_dim] of `dtype`, written at position L-1
+  // through the table before the attention reads it; null = no write
+  const void* key_new;
+  const void* value_new;
+  int64_t new_token_stride_bytes;
   // split-KV only
   int32_t partition_blocks;     // partition_size / 16
   int32_t max_parts;            // ceil(max_context_len / partition_size)

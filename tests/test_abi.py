@@ -164,6 +164,46 @@ def test_splitkv_fp8_workspace_checks():
     assert _decode_fp8(True, part=100) == SHAPE
 
 
+def _step(fp8=False, **kw):
+    a = dict(out=FAKE, query=FAKE, kn=FAKE, vn=FAKE, ts=4 * 128, k=FAKE, v=FAKE, block_stride=16 * 4 * 128,
+             num_blocks=32, bt=FAKE, bt_stride=3, lens=FAKE, B=4, hq=8, hkv=4, d=128, bs=16, scale=0.088,
+             ks=FAKE, vs=FAKE, dtype=2)
+    a.update(kw)
+    head = [a["out"], a["query"], a["kn"], a["vn"], a["ts"], a["k"], a["v"], a["block_stride"], a["num_blocks"],
+            a["bt"], a["bt_stride"], a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"]]
+    if fp8:
+        return P.lib().pa_decode_step_fp8(*head, a["ks"], a["vs"], a["dtype"], None)
+    return P.lib().pa_decode_step(*head, a["dtype"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), NULL), (dict(vn=None), NULL), (dict(out=None), NULL), (dict(ts=100), SHAPE),
+    (dict(ts=4 * 128 + 4), ALIGN), (dict(kn=MIS), ALIGN), (dict(d=96), UNSUP), (dict(B=0), OK),
+    (dict(B=0, kn=None), OK),
+])
+def test_decode_step_argument_checks(fp8, kw, code):
+    if fp8:
+        kw = dict(kw)
+        if "block_stride" not in kw:
+            kw["block_stride"] = 16 * 4 * 128
+    assert _step(fp8, **kw) == code
+
+
+def test_decode_step_fp8_specific_checks():
+    assert _step(True, dtype=0) == DTYPE
+    assert _step(True, ks=None) == NULL
+    assert _step(False, dtype=7) == DTYPE
+
+
+def test_graph_handle_checks():
+    lib = P.lib()
+    assert lib.pa_graph_begin(None, None) == NULL
+    assert lib.pa_graph_end(None) == NULL
+    assert lib.pa_graph_launch(None, None) == NULL
+    lib.pa_graph_destroy(None)                       # no-op
+
+
 def test_binding_raises_on_error_status():
     err = P.PagedAttentionError("pa_decode", 4)
     assert "PA_ERR_UNSUPPORTED" in str(err) and err.status == 4
