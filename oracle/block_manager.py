@@ -19,6 +19,10 @@ What it follows:
   copied only when one of them has to write into it (copy-on-write).
 * page "vLLM推理引擎深度实战" §5.3 (推理优化配置): a CPU swap space beside the
   GPU pool, i.e. whole blocks move between a device pool and a host pool.
+* page "vLLM 原理与源码阅读" (Prefix Caching → 自动检测与复用): the prompt content
+  is hashed into cache keys; a new request looks up the longest cached prefix;
+  only the uncached suffix needs its KV computed; the hit blocks are shared
+  through the block share counts.
 
 Reading taken where the pages leave a step open or contradict themselves:
 the §三 ``share_prefix`` listing can hand out a partly filled block and then
@@ -28,10 +32,22 @@ append: the manager reports the (source, destination) pair that the device
 must copy before the token is written, and the shared block's count drops by
 one. A full shared block needs no copy: the next token starts a new block.
 
+Prefix caching, readings: the cache works on whole blocks. The key of full
+block i of a prompt stands for the whole prefix tokens[0 : 16(i+1)] (here the
+tuple of those tokens itself, so keys never collide); partly filled blocks
+are never cached. A request's full prompt blocks enter the cache when the
+caller publishes them (after their KV is written); an entry that exists
+already keeps its block. A cached block whose count drops to zero stays
+cached while it waits in the free list; taking it from the free list for
+another use evicts its entry, and a cache hit on it takes it out of the
+free list. A hit never covers more blocks than the prompt has full blocks.
+
 Functions:
 
 * ``BlockManager``: allocate / append / fork / share_prefix / free / slots, with
-  the invariants checked by ``check_invariants``.
+  the invariants checked by ``check_invariants``; prefix caching through
+  ``allocate_cached`` (longest cached prefix, shared) and ``publish`` (a
+  request's full prompt blocks enter the cache).
 * ``copy_blocks``: for each (src, dst) pair, K and V of block dst become those
   of block src (the device copy that copy-on-write asks for); pairs with an
   index outside the pool are skipped.
@@ -62,6 +78,8 @@ class BlockManager:
         self.ref: List[int] = [0] * self.num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.cache: Dict[tuple, int] = {}          # whole-prefix key -> block
+        self.key_of: Dict[int, tuple] = {}         # block -> its cache key
 
     # -- taking and returning blocks (head of the free list out, tail in) --
     def _take(self) -> int:
@@ -69,6 +87,8 @@ class BlockManager:
             raise MemoryError("no free block")
         b = self.free.pop(0)
         self.ref[b] = 1
+        if b in self.key_of:                       # reused for other tokens: leaves the cache
+            del self.cache[self.key_of.pop(b)]
         return b
 
     def _drop(self, b: int) -> None:
@@ -120,6 +140,49 @@ class BlockManager:
         self.tables[child] = list(shared)
         self.lens[child] = int(num_tokens)
 
+    # -- prefix caching --
+    def prefix_keys(self, tokens: Sequence[int]) -> List[tuple]:
+        """Key of every full block of a prompt: the whole prefix up to the block's end."""
+        bs = self.block_size
+        return [tuple(int(t) for t in tokens[:bs * (i + 1)]) for i in range(len(tokens) // bs)]
+
+    def allocate_cached(self, seq: int, tokens: Sequence[int]) -> int:
+        """A new request for a prompt: the longest run of cached full blocks from its start
+        is shared, fresh blocks cover the rest, all or nothing. Returns the number of leading
+        tokens whose KV is already in the cache (a multiple of block_size)."""
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} exists")
+        hit = []
+        for key in self.prefix_keys(tokens):
+            if key not in self.cache:
+                break
+            hit.append(self.cache[key])
+        need = -(-len(tokens) // self.block_size) - len(hit)
+        idle = sum(1 for b in hit if self.ref[b] == 0)
+        if need > len(self.free) - idle:
+            raise MemoryError(f"need {need} blocks, {len(self.free) - idle} free")
+        for b in hit:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        self.tables[seq] = hit + [self._take() for _ in range(need)]
+        self.lens[seq] = len(tokens)
+        return len(hit) * self.block_size
+
+    def publish(self, seq: int, tokens: Sequence[int]) -> int:
+        """Enter the request's full blocks covering ``tokens`` (its first tokens, KV written)
+        into the cache; returns how many entries were added."""
+        n = min(len(tokens), self.lens[seq])
+        added = 0
+        for i, key in enumerate(self.prefix_keys(tokens[:n])):
+            b = self.tables[seq][i]
+            if key in self.cache or b in self.key_of:
+                continue
+            self.cache[key] = b
+            self.key_of[b] = key
+            added += 1
+        return added
+
     def free_seq(self, seq: int) -> None:
         for b in self.tables.pop(seq):
             self._drop(b)
@@ -140,6 +203,8 @@ class BlockManager:
         assert list(held) == self.ref, "share counts"
         assert sorted(self.free) == [b for b in range(self.num_blocks) if self.ref[b] == 0], "free list"
         assert len(set(self.free)) == len(self.free), "free list duplicates"
+        assert all(self.key_of[b] == k for k, b in self.cache.items()), "cache maps"
+        assert len(self.key_of) == len(self.cache), "cache maps"
 
 
 def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> Tuple[np.ndarray, np.ndarray]:
