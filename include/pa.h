@@ -368,6 +368,41 @@ PA_API int32_t pa_bm_free_list(const pa_block_manager* m, int32_t* out, int32_t 
 PA_API int32_t pa_bm_slots(const pa_block_manager* m, int64_t seq, int64_t pos0, int64_t count, int32_t* out);
 
 /*
+ * Prefix caching ([P2] Prefix Caching → 自动检测与复用: the prompt content is
+ * hashed into cache keys, a new request looks up the longest cached prefix,
+ * only the rest needs its KV computed, and the hit blocks are shared through
+ * the block counts). Block granular: the key of full block i of a prompt is a
+ * 64-bit FNV-1a hash chained over block i-1's key and the block's own token
+ * ids, standing for the whole prefix up to the block's end; a hit also checks
+ * the stored parent key and tokens exactly. Partly filled blocks are never
+ * cached.
+ *
+ *   pa_bm_allocate_cached  a new request for prompt `tokens` (int32 token ids,
+ *                  num_tokens of them): shares the longest run of cached full
+ *                  blocks from the prompt's start, takes fresh blocks from the
+ *                  head of the free list for the rest, all or nothing
+ *                  (PA_ERR_NO_BLOCKS changes nothing); *cached_tokens = the
+ *                  number of leading tokens whose KV is already cached (a
+ *                  multiple of block_size) — the caller computes and writes
+ *                  KV for positions >= *cached_tokens only
+ *   pa_bm_publish  enters the request's full blocks that hold tokens[0 ..
+ *                  num_tokens) (at most its length) into the cache, once their
+ *                  KV is written; a key already cached keeps its block, a
+ *                  block is cached under one key at most; *added (may be
+ *                  NULL) = entries added
+ *   pa_bm_num_cached  entries in the cache
+ * A cached block whose count drops to zero stays cached while it waits in the
+ * free list (a hit takes it back out); taken from the free list for other
+ * tokens it leaves the cache. Cached blocks are full, so appends never write
+ * into them.
+ */
+PA_API int32_t pa_bm_allocate_cached(pa_block_manager* m, int64_t seq, const int32_t* tokens, int64_t num_tokens,
+                              int64_t* cached_tokens);
+PA_API int32_t pa_bm_publish(pa_block_manager* m, int64_t seq, const int32_t* tokens, int64_t num_tokens,
+                      int32_t* added);
+PA_API int32_t pa_bm_num_cached(const pa_block_manager* m);
+
+/*
  * pa_prefill_chunked — a chunk of new query tokens per sequence attends over
  * the sequence's cache (prior tokens plus the chunk itself, already written
  * by pa_reshape_and_cache), on bf16/f16 matrix cores. The pages only name the

@@ -66,6 +66,9 @@ SIGNATURES = {
     "pa_bm_ref_count": (_i32, [_p, _i32]),
     "pa_bm_free_list": (_i32, [_p, _p, _i32]),
     "pa_bm_slots": (_i32, [_p, _i64, _i64, _i64, _p]),
+    "pa_bm_allocate_cached": (_i32, [_p, _i64, _p, _i64, _p]),
+    "pa_bm_publish": (_i32, [_p, _i64, _p, _i64, _p]),
+    "pa_bm_num_cached": (_i32, [_p]),
 }
 
 
@@ -444,3 +447,23 @@ class BlockManager:
         out = np.zeros(max(count, 1), dtype=np.int32)
         _check("pa_bm_slots", lib().pa_bm_slots(self._h, seq, pos0, count, out.ctypes.data_as(ctypes.c_void_p)))
         return out[:count].tolist()
+
+    def allocate_cached(self, seq: int, tokens) -> int:
+        """A new request for a prompt (token ids): shares the longest cached prefix; returns
+        the number of leading tokens whose KV is already cached."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int64(0)
+        _check("pa_bm_allocate_cached", lib().pa_bm_allocate_cached(
+            self._h, seq, t.ctypes.data_as(ctypes.c_void_p), t.size, ctypes.byref(cached)))
+        return cached.value
+
+    def publish(self, seq: int, tokens) -> int:
+        """Enter the request's full blocks holding ``tokens`` into the prefix cache."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        added = ctypes.c_int32(0)
+        _check("pa_bm_publish", lib().pa_bm_publish(self._h, seq, t.ctypes.data_as(ctypes.c_void_p), t.size,
+                                                    ctypes.byref(added)))
+        return added.value
+
+    def num_cached(self) -> int:
+        return int(lib().pa_bm_num_cached(self._h))

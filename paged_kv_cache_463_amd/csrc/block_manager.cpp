@@ -16,8 +16,21 @@
 // the shared block's count, and reports the (source, destination) pair that
 // pa_copy_blocks must copy before the token's K/V are scattered.
 //
+// Prefix caching (page "vLLM 原理与源码阅读", Prefix Caching → 自动检测与复用:
+// hash the prompt into cache keys, find the longest cached prefix, compute
+// only the rest, share the hit blocks), read at block granularity: the key of
+// full block i of a prompt is a 64-bit FNV-1a hash chained over the key of
+// block i-1 and the block's own tokens, so it stands for the whole prefix up
+// to the block's end; partly filled blocks are never cached. A hit also
+// compares the entry's stored parent key and tokens exactly, so a false match
+// needs two different prefixes whose keys collide in 64 bits. A request's
+// full prompt blocks enter the cache when the caller publishes them (after
+// their KV is written); an existing entry keeps its block. A cached block
+// whose count drops to zero stays cached in the free list; taking it from the
+// free list for other tokens evicts it, and a hit takes it back out of the
+// free list.
+//
 // Requests are keyed by 64-bit ids. A refused call changes nothing.
-#include <deque>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -31,20 +44,75 @@ struct pa_block_manager {
   };
   int32_t num_blocks = 0;
   int32_t block_size = 16;
-  std::deque<int32_t> free_list;            // head = front
+  // free list: doubly linked through block indices (a cache hit removes a
+  // block from anywhere in it); head = oldest
+  std::vector<int32_t> fnext, fprev;
+  std::vector<char> is_free;
+  int32_t fhead = -1, ftail = -1;
+  int32_t nfree = 0;
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  // prefix cache: key -> block; per cached block its key, parent key, tokens
+  std::unordered_map<uint64_t, int32_t> cache;
+  std::vector<char> cached;
+  std::vector<uint64_t> key_of, parent_of;
+  std::vector<int32_t> toks;                // num_blocks * block_size, filled on publish
 
+  void push_back(int32_t b) {
+    fnext[b] = -1;
+    fprev[b] = ftail;
+    if (ftail >= 0) fnext[ftail] = b; else fhead = b;
+    ftail = b;
+    is_free[b] = 1;
+    ++nfree;
+  }
+  void unlink(int32_t b) {
+    if (fprev[b] >= 0) fnext[fprev[b]] = fnext[b]; else fhead = fnext[b];
+    if (fnext[b] >= 0) fprev[fnext[b]] = fprev[b]; else ftail = fprev[b];
+    is_free[b] = 0;
+    --nfree;
+  }
+  void evict(int32_t b) {
+    if (!cached[b]) return;
+    cache.erase(key_of[b]);
+    cached[b] = 0;
+  }
   int32_t take() {
-    const int32_t b = free_list.front();
-    free_list.pop_front();
+    const int32_t b = fhead;
+    unlink(b);
     ref[b] = 1;
+    evict(b);                               // reused for other tokens
     return b;
   }
   void drop(int32_t b) {
-    if (--ref[b] == 0) free_list.push_back(b);
+    if (--ref[b] == 0) push_back(b);
   }
   int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+
+  // FNV-1a, 64 bit: offset basis 14695981039346656037, prime 1099511628211
+  static uint64_t fnv(uint64_t h, uint64_t v, int bytes) {
+    for (int i = 0; i < bytes; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= 1099511628211ull;
+    }
+    return h;
+  }
+  uint64_t block_key(uint64_t parent, const int32_t* t) const {
+    uint64_t h = fnv(14695981039346656037ull, parent, 8);
+    for (int32_t i = 0; i < block_size; ++i) h = fnv(h, (uint32_t)t[i], 4);
+    return h;
+  }
+  // the cached block for full block i of a prompt whose block i-1 has key
+  // `parent` (0 for i == 0), or -1
+  int32_t lookup(uint64_t parent, uint64_t key, const int32_t* t) const {
+    auto it = cache.find(key);
+    if (it == cache.end()) return -1;
+    const int32_t b = it->second;
+    if (parent_of[b] != parent) return -1;
+    for (int32_t i = 0; i < block_size; ++i)
+      if (toks[(int64_t)b * block_size + i] != t[i]) return -1;
+    return b;
+  }
 };
 
 extern "C" {
@@ -56,19 +124,23 @@ pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
   m->num_blocks = num_blocks;
   m->block_size = block_size;
   m->ref.assign(num_blocks, 0);
+  m->fnext.assign(num_blocks, -1);
+  m->fprev.assign(num_blocks, -1);
+  m->is_free.assign(num_blocks, 0);
+  m->cached.assign(num_blocks, 0);
+  m->key_of.assign(num_blocks, 0);
+  m->parent_of.assign(num_blocks, 0);
   if (free_order) {                         // must be a permutation of 0 .. num_blocks-1
-    std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
       const int32_t b = free_order[i];
-      if (b < 0 || b >= num_blocks || seen[b]) {
+      if (b < 0 || b >= num_blocks || m->is_free[b]) {
         delete m;
         return nullptr;
       }
-      seen[b] = 1;
-      m->free_list.push_back(b);
+      m->push_back(b);
     }
   } else {
-    for (int32_t b = 0; b < num_blocks; ++b) m->free_list.push_back(b);
+    for (int32_t b = 0; b < num_blocks; ++b) m->push_back(b);
   }
   return m;
 }
@@ -80,7 +152,7 @@ int32_t pa_bm_allocate(pa_block_manager* m, int64_t seq, int64_t num_tokens) {
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (m->seqs.count(seq)) return PA_ERR_SEQUENCE;
   const int64_t need = m->blocks_for(num_tokens);
-  if (need > (int64_t)m->free_list.size()) return PA_ERR_NO_BLOCKS;
+  if (need > m->nfree) return PA_ERR_NO_BLOCKS;
   pa_block_manager::Seq s;
   s.len = num_tokens;
   s.blocks.reserve(need);
@@ -98,10 +170,10 @@ int32_t pa_bm_append(pa_block_manager* m, int64_t seq, int64_t* slot, int32_t* c
   *cow_src = -1;
   *cow_dst = -1;
   if (pos % m->block_size == 0) {           // no block yet, or the last one is full
-    if (m->free_list.empty()) return PA_ERR_NO_BLOCKS;
+    if (m->nfree == 0) return PA_ERR_NO_BLOCKS;
     s.blocks.push_back(m->take());
   } else if (m->ref[s.blocks.back()] > 1) {  // shared and not full: copy before writing
-    if (m->free_list.empty()) return PA_ERR_NO_BLOCKS;
+    if (m->nfree == 0) return PA_ERR_NO_BLOCKS;
     const int32_t old = s.blocks.back();
     const int32_t fresh = m->take();
     m->drop(old);
@@ -143,7 +215,73 @@ int32_t pa_bm_free(pa_block_manager* m, int64_t seq) {
   return PA_OK;
 }
 
-int32_t pa_bm_num_free(const pa_block_manager* m) { return m ? (int32_t)m->free_list.size() : -1; }
+int32_t pa_bm_allocate_cached(pa_block_manager* m, int64_t seq, const int32_t* tokens, int64_t num_tokens,
+                              int64_t* cached_tokens) {
+  if (!m || !cached_tokens || (!tokens && num_tokens > 0)) return PA_ERR_NULL_PTR;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (m->seqs.count(seq)) return PA_ERR_SEQUENCE;
+  const int32_t bs = m->block_size;
+  std::vector<int32_t> hit;
+  uint64_t parent = 0;
+  for (int64_t i = 0; i < num_tokens / bs; ++i) {         // longest run of cached full blocks
+    const int32_t* t = tokens + i * bs;
+    const uint64_t key = m->block_key(parent, t);
+    const int32_t b = m->lookup(parent, key, t);
+    if (b < 0) break;
+    hit.push_back(b);
+    parent = key;
+  }
+  const int64_t need = m->blocks_for(num_tokens) - (int64_t)hit.size();
+  int64_t idle = 0;
+  for (int32_t b : hit) idle += m->ref[b] == 0;
+  if (need > m->nfree - idle) return PA_ERR_NO_BLOCKS;
+  pa_block_manager::Seq s;
+  s.len = num_tokens;
+  s.blocks.reserve(hit.size() + need);
+  for (int32_t b : hit) {
+    if (m->ref[b] == 0) m->unlink(b);
+    ++m->ref[b];
+    s.blocks.push_back(b);
+  }
+  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(m->take());
+  m->seqs.emplace(seq, std::move(s));
+  *cached_tokens = (int64_t)hit.size() * bs;
+  return PA_OK;
+}
+
+int32_t pa_bm_publish(pa_block_manager* m, int64_t seq, const int32_t* tokens, int64_t num_tokens,
+                      int32_t* added) {
+  if (!m || (!tokens && num_tokens > 0)) return PA_ERR_NULL_PTR;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  auto it = m->seqs.find(seq);
+  if (it == m->seqs.end()) return PA_ERR_SEQUENCE;
+  const pa_block_manager::Seq& s = it->second;
+  const int32_t bs = m->block_size;
+  const int64_t n = num_tokens < s.len ? num_tokens : s.len;
+  if (m->toks.empty() && n >= bs) m->toks.assign((size_t)m->num_blocks * bs, 0);
+  int32_t count = 0;
+  uint64_t parent = 0;
+  for (int64_t i = 0; i < n / bs; ++i) {
+    const int32_t* t = tokens + i * bs;
+    const uint64_t key = m->block_key(parent, t);
+    const int32_t b = s.blocks[i];
+    if (!m->cache.count(key) && !m->cached[b]) {
+      m->cache.emplace(key, b);
+      m->cached[b] = 1;
+      m->key_of[b] = key;
+      m->parent_of[b] = parent;
+      for (int32_t k = 0; k < bs; ++k) m->toks[(int64_t)b * bs + k] = t[k];
+      ++count;
+    }
+    parent = key;
+  }
+  if (added) *added = count;
+  return PA_OK;
+}
+
+int32_t pa_bm_num_cached(const pa_block_manager* m) { return m ? (int32_t)m->cache.size() : -1; }
+
+int32_t pa_bm_num_free(const pa_block_manager* m) { return m ? m->nfree : -1; }
 
 int64_t pa_bm_seq_len(const pa_block_manager* m, int64_t seq) {
   if (!m) return -1;
@@ -168,10 +306,11 @@ int32_t pa_bm_ref_count(const pa_block_manager* m, int32_t block) {
 
 int32_t pa_bm_free_list(const pa_block_manager* m, int32_t* out, int32_t capacity) {
   if (!m) return -1;
-  const int32_t n = (int32_t)m->free_list.size();
-  if (out)
-    for (int32_t i = 0; i < n && i < capacity; ++i) out[i] = m->free_list[i];
-  return n;
+  if (out) {
+    int32_t i = 0;
+    for (int32_t b = m->fhead; b >= 0 && i < capacity; b = m->fnext[b]) out[i++] = b;
+  }
+  return m->nfree;
 }
 
 int32_t pa_bm_slots(const pa_block_manager* m, int64_t seq, int64_t pos0, int64_t count, int32_t* out) {

@@ -86,3 +86,78 @@ def test_library_manager_argument_checks():
             call()
         assert e.value.status == status
     assert bm.num_free() == 2 and bm.block_table(7) == [0, 1]
+
+
+def run_both_prefix(seed, num_blocks=40, steps=400):
+    """The same seeded mix of prefix-cached allocations, publishes, appends, forks and frees
+    on both managers; returns, tables, counts, free lists and cache sizes must agree."""
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(num_blocks)
+    ref = OBM.BlockManager(num_blocks, free_order=order)
+    lib = P.BlockManager(num_blocks, free_order=order)
+    sp0 = [int(x) for x in rng.integers(0, 50, 48)]
+    systems = [sp0, sp0[:16] + [int(x) for x in rng.integers(0, 50, 24)], [999] * 16 + sp0[16:]]
+    toks, nxt, hits = {}, 0, 0
+    for _ in range(steps):
+        op = int(rng.integers(0, 10))
+        live = list(toks)
+        if op < 4 or not live:
+            sp = systems[int(rng.integers(0, 3))]
+            prompt = sp[:int(rng.integers(0, len(sp) + 1))] + [int(x) for x in rng.integers(0, 50, int(rng.integers(0, 20)))]
+            try:
+                a = ref.allocate_cached(nxt, prompt)
+            except MemoryError:
+                with pytest.raises(P.PagedAttentionError) as e:
+                    lib.allocate_cached(nxt, prompt)
+                assert e.value.status == 8
+            else:
+                assert lib.allocate_cached(nxt, prompt) == a
+                hits += a > 0
+                toks[nxt] = prompt
+                if rng.random() < 0.8:
+                    assert lib.publish(nxt, prompt) == ref.publish(nxt, prompt)
+            nxt += 1
+        elif op < 6:
+            s = live[int(rng.integers(0, len(live)))]
+            try:
+                r = ref.append(s)
+            except MemoryError:
+                with pytest.raises(P.PagedAttentionError):
+                    lib.append(s)
+            else:
+                assert lib.append(s) == r
+        elif op < 7:
+            s = live[int(rng.integers(0, len(live)))]
+            ref.fork(s, nxt)
+            lib.fork(s, nxt)
+            toks[nxt] = toks[s]
+            nxt += 1
+        else:
+            s = live[int(rng.integers(0, len(live)))]
+            ref.free_seq(s)
+            lib.free(s)
+            del toks[s]
+        ref.check_invariants()
+        for s in toks:
+            assert lib.block_table(s) == ref.tables[s]
+        assert [lib.ref_count(b) for b in range(num_blocks)] == ref.ref
+        assert lib.free_list() == ref.free
+        assert lib.num_cached() == len(ref.cache)
+    return hits
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_library_prefix_cache_matches_oracle(seed):
+    assert run_both_prefix(seed) > 0
+
+
+def test_library_prefix_cache_argument_checks():
+    bm = P.BlockManager(4)
+    bm.allocate_cached(1, list(range(20)))
+    for call, status in [(lambda: bm.allocate_cached(1, [1]), 9), (lambda: bm.publish(5, [1]), 9),
+                         (lambda: bm.allocate_cached(2, list(range(70))), 8)]:
+        with pytest.raises(P.PagedAttentionError) as e:
+            call()
+        assert e.value.status == status
+    assert bm.publish(1, list(range(20))) == 1 and bm.num_cached() == 1
+    assert bm.publish(1, list(range(20))) == 0                # already cached

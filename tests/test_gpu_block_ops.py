@@ -152,3 +152,52 @@ def test_copy_on_write_decode_step():
     assert_close(out_f64(out), ref, "bf16", "copy-on-write decode")
     # the two requests differ only in their last token: their outputs differ
     assert not torch.equal(out[0], out[1])
+
+
+def test_prefix_cache_feeds_decode():
+    """Requests get their tables from the library's prefix cache; only the positions the cache
+    does not cover are computed and scattered; decode over the shared blocks equals the oracle
+    on each request's own, unshared K/V. A token's K/V rows are a seeded function of its whole
+    prefix (as real K/V are), so a request that read another prefix's rows would differ."""
+    hq, hkv, d, nb = 8, 2, 64, 64
+
+    def kv_rows(prefix):
+        r = np.random.default_rng(abs(hash(tuple(prefix))) % (1 << 32))
+        return (r.standard_normal((2, hkv, d)).astype(np.float32))
+
+    rng = np.random.default_rng(29)
+    system = [int(x) for x in rng.integers(0, 100, 48)]
+    prompts = [system + [int(x) for x in rng.integers(0, 100, n)] for n in (5, 17, 0, 30)]
+    prompts.append(system[:20] + [7, 7, 7])                  # shares one full block only
+    bm = P.BlockManager(nb)
+    kd = torch.zeros((nb, 16, hkv, d), dtype=torch.float32, device="cuda")
+    vd = torch.zeros_like(kd)
+    cached = []
+    for s, prompt in enumerate(prompts):
+        c = bm.allocate_cached(s, prompt)
+        cached.append(c)
+        pos = list(range(c, len(prompt)))
+        rows = np.stack([kv_rows(prompt[:p + 1]) for p in pos]) if pos else np.zeros((0, 2, hkv, d), np.float32)
+        if pos:
+            P.reshape_and_cache(torch.from_numpy(rows[:, 0].copy()).cuda(), torch.from_numpy(rows[:, 1].copy()).cuda(),
+                                kd, vd, torch.tensor(bm.slots(s, c, len(pos)), dtype=torch.int32, device="cuda"))
+        bm.publish(s, prompt)
+    assert cached == [0, 48, 48, 48, 16]
+    B = len(prompts)
+    lens = np.array([len(p) for p in prompts], np.int32)
+    tables = np.full((B, 8), -1, np.int32)
+    for s in range(B):
+        t = bm.block_table(s)
+        tables[s, :len(t)] = t
+    q = rng.standard_normal((B, hq, d)).astype(np.float32)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    say("case: prefix-cached tables feed decode")
+    P.decode(out, torch.from_numpy(q).cuda(), kd, vd, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+             d ** -0.5)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    for s, prompt in enumerate(prompts):                      # each request on its own dense K/V
+        rows = np.stack([kv_rows(prompt[:p + 1]) for p in range(len(prompt))]).astype(np.float64)
+        for h in range(hq):
+            ref = oracle.attend(q[s, h].astype(np.float64), rows[:, 0, h // 4], rows[:, 1, h // 4], d ** -0.5)
+            assert np.abs(got[s, h] - ref).max() <= 1e-5, f"request {s} head {h}"
