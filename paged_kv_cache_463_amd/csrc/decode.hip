@@ -45,6 +45,8 @@
 // are handed out by a work counter (see split_work).
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -53,6 +55,9 @@
 #endif
 #ifndef PA_SPLITKV_WAVES
 #define PA_SPLITKV_WAVES 4
+#endif
+#ifndef PA_DECODE_ROTATE
+#define PA_DECODE_ROTATE 1
 #endif
 
 namespace pa {
@@ -317,14 +322,147 @@ __global__ void splitkv_reset_kernel(int32_t* ctr) {
   if (threadIdx.x == 0) *ctr = 0;
 }
 
+// Split-KV with workgroup items. When every sequence has only a few
+// partitions (short and mixed contexts), a partition walked by one wave is too
+// little work per wave, while one workgroup per sequence leaves the longest
+// sequence running alone at the end. Here one workgroup takes one (kv head,
+// sequence, partition) item at a time, its W waves share the partition's
+// blocks round-robin as in the single pass, and a sequence with a single
+// partition writes its output directly (only longer ones go through the
+// workspace and the merge). Workgroups are persistent: each takes items from
+// the work counter until none is left, so the grid only has to fill the chip.
+// Items are numbered kv head fastest, then sequence by sequence in descending
+// length (the ranking of the single pass) and partition by partition, so the
+// largest items are taken first and the last ones are the shortest. Every
+// workgroup builds that numbering once in LDS: the rank order perm[] and the
+// exclusive prefix sums pre[] of the partition counts in rank order. Batches
+// above kRankMaxSeqs sequences number all num_seqs * max_parts pairs in
+// sequence order instead (empty pairs are skipped).
+enum : int { kSingle = 0, kWaveItems = 1, kGroupItems = 2 };
+constexpr int kPlanCur = kBuckets;                       // [0, kBuckets): bucket bases
+constexpr int kPlanPre = 2 * kBuckets;                   // bucket members, then pre[0..B]
+constexpr int kPlanPerm = kPlanPre + kRankMaxSeqs + 1;   // perm[rank] = sequence
+constexpr int kPlanTicket = kPlanPerm + kRankMaxSeqs;
+constexpr int kPlanInts = kPlanTicket + 1;
+
+__device__ __forceinline__ int parts_of(const DecodeParams& p, int L) {
+  const int nb = min((max(L, 0) + kBlockSize - 1) / kBlockSize, p.block_table_stride);
+  return (nb + p.partition_blocks - 1) / p.partition_blocks;
+}
+
+// 64 lanes turn v[0..n) into its exclusive prefix sums in place, v[n] = total.
+__device__ __forceinline__ void wave_exclusive_scan(int* v, int n) {
+  const int l = threadIdx.x & 63;
+  const int per = (n + 63) / 64;
+  const int t0 = min(l * per, n), t1 = min(t0 + per, n);
+  int run = 0;
+  for (int t = t0; t < t1; ++t) run += v[t];
+  int inc = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (l >= o) inc += y;
+  }
+  int acc = inc - run;
+  for (int t = t0; t < t1; ++t) {
+    const int c = v[t];
+    v[t] = acc;
+    acc += c;
+  }
+  if (l == 63) v[n] = inc;
+}
+
+template <int NT>
+__device__ __forceinline__ void group_plan(const DecodeParams& p, int* s) {
+  static_assert(NT >= kBuckets / 2, "one scan wave covers the buckets");
+  const int B = p.num_seqs;
+  if (B > kRankMaxSeqs) return;
+  const int32_t* lens = p.context_lens;
+  int* base = s;
+  int* cur = s + kPlanCur;
+  int* key = s + kPlanPre;
+  int* perm = s + kPlanPerm;
+  for (int i = threadIdx.x; i < kBuckets; i += NT) cur[i] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) atomicAdd(&cur[length_bucket(lens[t])], 1);
+  __syncthreads();
+  if (threadIdx.x < 64) {                                        // bucket bases, 2 buckets a lane
+    const int l = threadIdx.x;
+    const int c0 = cur[2 * l], c1 = cur[2 * l + 1];
+    int inc = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (l >= o) inc += y;
+    }
+    const int exc = inc - c0 - c1;
+    base[2 * l] = exc;
+    base[2 * l + 1] = exc + c0;
+    cur[2 * l] = exc;
+    cur[2 * l + 1] = exc + c0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) {                    // gather bucket members
+    const int L = lens[t];
+    key[atomicAdd(&cur[length_bucket(L)], 1)] = rank_key(L, t);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += NT) {                    // rank inside the bucket
+    const int L = lens[t];
+    const int k = length_bucket(L), kk = rank_key(L, t);
+    const int lo = base[k], hi = cur[k];
+    int rank = lo;
+    for (int j = lo; j < hi; ++j) rank += key[j] > kk;
+    perm[rank] = t;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < B; r += NT) key[r] = parts_of(p, lens[perm[r]]);
+  __syncthreads();
+  if (threadIdx.x < 64) wave_exclusive_scan(key, B);
+  __syncthreads();
+}
+
+// Next item of this workgroup: false when the counter has passed the last one.
+template <int NT>
+__device__ __forceinline__ bool group_work(const DecodeParams& p, int* s, int& g, int& b, int& part,
+                                           int& np) {
+  if (threadIdx.x == 0) s[kPlanTicket] = atomicAdd(p.ws_ctr, 1);
+  __syncthreads();
+  const int ticket = __builtin_amdgcn_readfirstlane(s[kPlanTicket]);
+  g = ticket % p.num_kv_heads;
+  const int item = ticket / p.num_kv_heads;
+  const int B = p.num_seqs;
+  if (B > kRankMaxSeqs) {
+    b = item / p.max_parts;
+    part = item % p.max_parts;
+    if (b >= B) return false;
+    np = parts_of(p, p.context_lens[b]);
+    return true;
+  }
+  const int* pre = s + kPlanPre;
+  if (item >= __builtin_amdgcn_readfirstlane(pre[B])) return false;
+  int lo = 0, hi = B - 1;                   // last rank whose first item is <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid; else hi = mid - 1;
+  }
+  const int first = __builtin_amdgcn_readfirstlane(pre[lo]);
+  b = __builtin_amdgcn_readfirstlane(s[kPlanPerm + lo]);
+  part = item - first;
+  np = __builtin_amdgcn_readfirstlane(pre[lo + 1]) - first;
+  return true;
+}
+
 // A lane's cache slice of one token row: 16 bytes of a 16-bit or fp32 cache,
 // or the 8 bytes of an FP8 cache that hold the same EPL elements.
 template <DT kt> struct KvRaw { using type = u32x4; };
 template <> struct KvRaw<DT::FP8> { using type = u32x2; };
 
-template <DT dt, DT kt, int D, int G, int W, bool SPLIT, int NB>
+template <DT dt, DT kt, int D, int G, int W, int MODE, int NB>
 __global__ __launch_bounds__(64 * W)
 void decode_kernel(DecodeParams p) {
+  constexpr bool SPLIT = MODE != kSingle;
+  constexpr bool GROUP = MODE == kGroupItems;
   constexpr bool F8 = kt == DT::FP8;        // e4m3 cache, widened to dt on the fly
   static_assert(F8 || kt == dt, "a 16-bit or fp32 cache has the query's type");
   static_assert(!F8 || dt != DT::F32, "an fp8 cache is read with 16-bit queries");
@@ -343,6 +481,7 @@ void decode_kernel(DecodeParams p) {
   __shared__ float s_acc[W][G][D];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
+  __shared__ int s_plan[GROUP ? kPlanInts : 1];
 
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep the
@@ -351,9 +490,14 @@ void decode_kernel(DecodeParams p) {
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int own = HM::owner(c);
-  int g, b, part = 0;
-  if constexpr (SPLIT) {
+  if constexpr (GROUP) group_plan<64 * W>(p, s_plan);
+  // one trip, except with workgroup items: then one trip per item
+  for (;;) {
+  int g, b, part = 0, np = 1;
+  if constexpr (MODE == kWaveItems) {
     if (!split_work<64 * W>(p, wave, g, b, part)) return;   // no work item left
+  } else if constexpr (GROUP) {
+    if (!group_work<64 * W>(p, s_plan, g, b, part, np)) return;
   } else {
     g = blockIdx.x;
     b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
@@ -365,7 +509,7 @@ void decode_kernel(DecodeParams p) {
   // slot the table names for position L-1, as the append rule puts it) and a
   // barrier, whose workgroup-scope fences order the stores before every
   // wave's loads, separates the write from the attention.
-  if constexpr (!SPLIT) {
+  if constexpr (MODE == kSingle) {
     if (p.key_new) {                        // uniform: a kernel argument
       const int pos = p.context_lens[b] - 1;
       constexpr int NCH = D / 8;            // 8-element chunks of one head's row
@@ -399,13 +543,20 @@ void decode_kernel(DecodeParams p) {
 
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-  // single pass: the W waves share the sequence's blocks round-robin.
-  // split-KV: every wave walks one partition on its own (no merge across waves)
-  constexpr int STEP = SPLIT ? 1 : W;
+  // single pass and workgroup items: the W waves share the blocks round-robin.
+  // wave items: every wave walks one partition on its own (no merge across waves)
+  constexpr int STEP = MODE == kWaveItems ? 1 : W;
   int lo = 0, hi = nblk;
   if constexpr (SPLIT) {
     lo = part * p.partition_blocks;
-    if (lo >= nblk) return;                 // only where empty pairs are numbered too
+    if (lo >= nblk) {                       // only where empty pairs are numbered too
+      if constexpr (GROUP) {
+        __syncthreads();                    // every wave has read the ticket
+        continue;
+      } else {
+        return;
+      }
+    }
     hi = min(nblk, lo + p.partition_blocks);
   }
 
@@ -447,7 +598,19 @@ void decode_kernel(DecodeParams p) {
   // unconditionally (a conditional load would make the compiler's wait counts
   // drain the prefetch of every block), and re-reading the block a wave has
   // just read is an L2 hit.
-  auto block_id = [&](int i) -> int { return tbl[min(i, hi - 1)]; };
+  // Walk order: with PA_DECODE_ROTATE the waves of a workgroup start at a
+  // per-sequence offset into the blocks and wrap around, so sequences that
+  // share physical blocks do not all read them at the same moment. Scores
+  // and masks follow the logical block, so only the summation order changes.
+  int rot = 0;
+#if PA_DECODE_ROTATE
+  if constexpr (MODE != kWaveItems) {
+    const int span = hi - lo;
+    rot = span > 1 ? (int)(((uint32_t)b * 2654435761u) >> 8) % span : 0;
+  }
+#endif
+  auto logical = [&](int i) -> int { return i + rot >= hi ? i + rot - (hi - lo) : i + rot; };
+  auto block_id = [&](int i) -> int { return tbl[logical(min(i, hi - 1))]; };
   auto load_kv = [](const char* a) -> KR {
     if constexpr (F8) return load8(a);
     else return load16(a);
@@ -485,7 +648,7 @@ void decode_kernel(DecodeParams p) {
     // copies, no early wait on the V loads).
     // An fp8 cache pairs bytes instead: [c j, c j+1, c+1 j, c+1 j+1] for
     // columns (4i, 4i+1) and (4i+2, 4i+3) of one dword, before widening.
-    const int tok0 = i * kBlockSize;
+    const int tok0 = logical(i) * kBlockSize;
     constexpr uint32_t kSelLo = F8 ? 0x05010400u : 0x05040100u;   // column 2i of tokens (j, j+1)
     constexpr uint32_t kSelHi = F8 ? 0x07030602u : 0x07060302u;   // column 2i+1
     constexpr uint32_t kKeepJ1 = F8 ? 0xFF00FF00u : 0xFFFF0000u;  // selector bytes of token j+1
@@ -604,7 +767,7 @@ void decode_kernel(DecodeParams p) {
   // to be used.
   KR kbuf[NB][TPL], vbuf[NB][TPL];
   bool okb[NB];
-  const int first = SPLIT ? lo : lo + wave;
+  const int first = MODE == kWaveItems ? lo : lo + wave;
   if (first < hi) {
     // buffers issued in order (an empty asm that clobbers memory keeps the
     // loads of buffer k+1 behind those of buffer k), as inside the loop
@@ -654,7 +817,7 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] *= vs;
   }
-  if constexpr (SPLIT) {                    // the wave's partial goes straight to the workspace
+  if constexpr (MODE == kWaveItems) {       // the wave's partial goes straight to the workspace
     if (r == 0) {
       const int64_t row0 = (int64_t)b * p.num_q_heads + hq0;
 #pragma unroll
@@ -697,7 +860,19 @@ void decode_kernel(DecodeParams p) {
       den = fmaf(sc, s_l[w][h], den);
     }
     const int64_t row = (int64_t)b * p.num_q_heads + hq0 + h;
-    store_elem<dt>(p.out, row * D + d, den > 0.f ? num / den : 0.f);
+    if (GROUP && np > 1) {                  // a partition of a longer sequence: to the merge
+      const int64_t pr = row * p.max_parts + part;
+      p.ws_acc[pr * D + d] = num;
+      if (d == 0) {
+        p.ws_ml[2 * pr] = M;
+        p.ws_ml[2 * pr + 1] = den;
+      }
+    } else {
+      store_elem<dt>(p.out, row * D + d, den > 0.f ? num / den : 0.f);
+    }
+  }
+  if constexpr (!GROUP) return;
+  __syncthreads();                          // s_acc, s_m, s_l and the ticket are reused
   }
 }
 
@@ -708,7 +883,7 @@ void decode_kernel(DecodeParams p) {
 //   M = max_p m_p,  w_p = 2^(m_p - M),  o = sum_p w_p acc_p / sum_p w_p l_p.
 constexpr int kMergeThreads = 256;
 
-template <DT dt, int D>
+template <DT dt, int D, bool DIRECT1>
 __global__ __launch_bounds__(kMergeThreads)
 void splitkv_merge_kernel(DecodeParams p) {
   constexpr int TPR = D / 4;                       // threads per partition row
@@ -721,6 +896,7 @@ void splitkv_merge_kernel(DecodeParams p) {
   const int L = max(p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   const int np = min((nblk + p.partition_blocks - 1) / p.partition_blocks, p.max_parts);
+  if (DIRECT1 && np == 1) return;                  // written by the partition pass itself
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
   const float* ml = p.ws_ml + row * p.max_parts * 2;
   const float* pa_ = p.ws_acc + row * p.max_parts * D;
@@ -778,64 +954,96 @@ constexpr int decode_buffers(DT dt, DT kt, int D, int G) {
 
 // Waves per workgroup; fp32 with head_dim 128 holds twice the bytes per lane
 // and stays at 4 waves so that its registers fit without spilling.
-template <DT dt, int D, bool SPLIT>
+template <DT dt, int D, int MODE>
 constexpr int decode_waves() {
-  return (dt == DT::F32 && D == 128) ? 4 : (SPLIT ? PA_SPLITKV_WAVES : PA_DECODE_WAVES);
+  return (dt == DT::F32 && D == 128) ? 4 : (MODE == kWaveItems ? PA_SPLITKV_WAVES : PA_DECODE_WAVES);
 }
 
-template <DT dt, DT kt, int D, bool SPLIT>
-static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
-  constexpr int W = decode_waves<dt, D, SPLIT>();
-  const int G = p.num_q_heads / p.num_kv_heads;
+// Split-KV takes workgroup items when no sequence has more than this many
+// partitions (short or mixed contexts); beyond it nearly every item is a whole
+// partition and one wave per item needs no merge across waves.
+#ifndef PA_GROUP_MAX_PARTS
+#define PA_GROUP_MAX_PARTS 16
+#endif
+
+// Persistent grid of the workgroup-item kernel: as many workgroups as the chip
+// holds at once, never more than there can be items.
+template <typename K>
+static int64_t resident_grid(K kernel, int threads, int64_t items) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return -1;
+  return std::min<int64_t>(items, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
+}
+
+template <DT dt, DT kt, int D, int G, int MODE>
+static hipError_t launch_mode(const DecodeParams& p, hipStream_t s) {
+  constexpr int W = decode_waves<dt, D, MODE>();
+  auto kernel = decode_kernel<dt, kt, D, G, W, MODE, decode_buffers(dt, kt, D, G)>;
   dim3 grid(p.num_kv_heads, p.num_seqs, 1);
-  if constexpr (SPLIT) {                   // work items are handed out by a counter
-    hipLaunchKernelGGL(splitkv_reset_kernel, dim3(1), dim3(64), 0, s, p.ws_ctr);
+  if constexpr (MODE != kSingle) {          // work items are handed out by a counter
     const int64_t items = (int64_t)p.num_kv_heads * p.num_seqs * p.max_parts;
-    const int64_t wgs = (items + items / 4 + W - 1) / W;
-    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-    grid = dim3((unsigned)wgs);
+    if (items + items / 4 + 64 * W > 0x7FFFFFFF) return hipErrorInvalidValue;   // tickets fit int32
+    hipLaunchKernelGGL(splitkv_reset_kernel, dim3(1), dim3(64), 0, s, p.ws_ctr);
+    int64_t wgs;
+    if constexpr (MODE == kGroupItems) {
+      wgs = resident_grid(kernel, 64 * W, items);
+      if (wgs < 0) return hipErrorInvalidValue;
+    } else {
+      wgs = (items + items / 4 + W - 1) / W;
+    }
+    grid = dim3((unsigned)std::max<int64_t>(wgs, 1));
   }
-  dim3 block(64 * W);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 1, W, SPLIT, decode_buffers(dt, kt, D, 1)>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 2, W, SPLIT, decode_buffers(dt, kt, D, 2)>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 4, W, SPLIT, decode_buffers(dt, kt, D, 4)>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<dt, kt, D, 8, W, SPLIT, decode_buffers(dt, kt, D, 8)>), grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !SPLIT) return e;
-  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D>), dim3(p.num_q_heads, p.num_seqs), dim3(kMergeThreads), 0, s, p);
+  if (e != hipSuccess || MODE == kSingle) return e;
+  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D, MODE == kGroupItems>), dim3(p.num_q_heads, p.num_seqs),
+                     dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <DT dt, DT kt, int D, int MODE>
+static hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+  switch (p.num_q_heads / p.num_kv_heads) {
+    case 1: return launch_mode<dt, kt, D, 1, MODE>(p, s);
+    case 2: return launch_mode<dt, kt, D, 2, MODE>(p, s);
+    case 4: return launch_mode<dt, kt, D, 4, MODE>(p, s);
+    case 8: return launch_mode<dt, kt, D, 8, MODE>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int MODE>
 static hipError_t launch_any(const DecodeParams& p, hipStream_t s) {
   const DT dt = static_cast<DT>(p.dtype);
   if (static_cast<DT>(p.kv_dtype) == DT::FP8) {
     if (p.head_dim == 128) {
-      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 128, SPLIT>(p, s);
-      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 128, SPLIT>(p, s);
+      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 128, MODE>(p, s);
+      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 128, MODE>(p, s);
     } else if (p.head_dim == 64) {
-      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 64, SPLIT>(p, s);
-      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 64, SPLIT>(p, s);
+      if (dt == DT::F16) return launch_g<DT::F16, DT::FP8, 64, MODE>(p, s);
+      if (dt == DT::BF16) return launch_g<DT::BF16, DT::FP8, 64, MODE>(p, s);
     }
     return hipErrorInvalidValue;
   }
   if (p.kv_dtype != p.dtype) return hipErrorInvalidValue;
   if (p.head_dim == 128) {
-    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 128, SPLIT>(p, s);
-    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 128, SPLIT>(p, s);
-    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 128, SPLIT>(p, s);
+    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 128, MODE>(p, s);
+    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 128, MODE>(p, s);
+    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 128, MODE>(p, s);
   } else if (p.head_dim == 64) {
-    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 64, SPLIT>(p, s);
-    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 64, SPLIT>(p, s);
-    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 64, SPLIT>(p, s);
+    if (dt == DT::F32) return launch_g<DT::F32, DT::F32, 64, MODE>(p, s);
+    if (dt == DT::F16) return launch_g<DT::F16, DT::F16, 64, MODE>(p, s);
+    if (dt == DT::BF16) return launch_g<DT::BF16, DT::BF16, 64, MODE>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s) { return launch_any<false>(p, s); }
-hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s) { return launch_any<true>(p, s); }
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s) { return launch_any<kSingle>(p, s); }
+hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s) {
+  return p.max_parts <= PA_GROUP_MAX_PARTS ? launch_any<kGroupItems>(p, s) : launch_any<kWaveItems>(p, s);
+}
 
 }  // namespace pa

@@ -68,12 +68,14 @@ class DeviceDecode:
     def scatter(self):
         P.reshape_and_cache(self.kn, self.vn, self.kp, self.vp, self.slots)
 
-    def decode(self, split: int = 0, workspace=None, out=None):
+    def decode(self, split: int = 0, workspace=None, out=None, mcl=None):
+        """``mcl`` overrides the max_context_len passed to split-KV (any bound >= the longest
+        sequence is valid; a larger one raises the partition count the library plans for)."""
         out = self.out if out is None else out
         c = self.case
         if split:
             P.decode_splitkv(out, self.q, self.kp, self.vp, self.bt, self.lens, c.scale,
-                             max(c.max_context_len, 1), split, workspace)
+                             max(c.max_context_len, 1) if mcl is None else mcl, split, workspace)
         else:
             P.decode(out, self.q, self.kp, self.vp, self.bt, self.lens, c.scale)
         return out

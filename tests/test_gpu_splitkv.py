@@ -1,4 +1,11 @@
-"""GPU parity of pa_decode_splitkv (partition pass + log-sum-exp merge) through the C ABI."""
+"""GPU parity of pa_decode_splitkv (partition pass + log-sum-exp merge) through the C ABI.
+
+The library plans in one of two ways from max_context_len / partition_size: up to 16 partitions
+per sequence, a workgroup walks one (kv head, sequence, partition) item and a sequence with a
+single partition is written directly; above that, one wave walks one partition and every
+sequence goes through the merge. Tests name the mode they reach; passing a max_context_len
+above the longest sequence (a valid bound) raises the planned partition count and forces the
+wave mode on the same inputs."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype,G,D", [("bf16", 8, 128), ("f16", 1, 128), ("f32", 4, 64), ("bf16", 2, 64)])
-@pytest.mark.parametrize("part", [16, 64, 512])
+@pytest.mark.parametrize("part", [16, 64, 512])     # 94 and 24 partitions: wave items; 3: workgroup items
 def test_splitkv_shapes(dtype, G, D, part):
     hkv = 2 if G < 8 else 1
     case = W.make_decode("split", dtype, [1, 16, 17, 100, 511, 512, 513, 1500], G * hkv, hkv, D,
@@ -25,35 +32,91 @@ def test_splitkv_shapes(dtype, G, D, part):
     assert_close(out_f64(out), oracle_decode(case, kp, vp), dtype, f"splitkv part={part}")
 
 
-def test_splitkv_batch_above_dense_numbering_limit():
+@pytest.mark.parametrize("mode,span,part", [("group", 97, 32), ("wave", 297, 16)])
+def test_splitkv_batch_above_dense_numbering_limit(mode, span, part):
     """Above 1024 sequences the work items number every (sequence, partition) pair, empty ones
-    included; every output row must still be written once and right (the output starts NaN)."""
-    lens = [(13 * i) % 97 + 1 for i in range(1100)]
+    included; every output row must still be written once and right (the output starts NaN).
+    Lengths up to 97 in 32-token partitions plan 4 partitions (workgroup items); up to 297 in
+    16-token partitions, 19 (wave items)."""
+    lens = [(13 * i) % span + 1 for i in range(1100)]
     case = W.make_decode("splitbig", "bf16", lens, 4, 2, 64, seed=41)
-    say(f"case: splitkv B={case.num_seqs} part=32")
+    say(f"case: splitkv {mode} items B={case.num_seqs} part={part}")
     d = DeviceDecode(case)
     d.scatter()
-    out = d.decode(split=32)
+    out = d.decode(split=part)
     torch.cuda.synchronize()
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     assert_close(out_f64(out), oracle_decode(case, kp, vp), "bf16", "splitkv B=1100")
 
 
 def test_single_partition_agrees_with_single_pass():
-    """A partition covering the whole sequence is the same softmax as the single pass. The split
-    pass sums a partition in one wave while the single pass merges four waves, so the two agree
-    to rounding (and each with the oracle), not bit for bit."""
+    """A partition covering the whole sequence is the same softmax as the single pass. With
+    workgroup items it is also the same decomposition (four waves taking the blocks
+    round-robin, the same merge of the waves, the output written directly), so the bits agree.
+    With wave items (forced by a larger max_context_len) one wave sums the partition and the
+    merge normalises it, so that result agrees to rounding (and with the oracle), not bit for bit."""
     case = W.make_decode("onepart", "bf16", [3, 90, 400, 1000], 32, 8, 128, seed=31)
     d = DeviceDecode(case)
     d.scatter()
     a = d.decode().clone()
-    b = d.decode(split=1024, out=torch.empty_like(a))
+    b = d.decode(split=1024, out=torch.full_like(a, float("nan")))
+    c = d.decode(split=1024, out=torch.full_like(a, float("nan")), mcl=17 * 1024)
     torch.cuda.synchronize()
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     ref = oracle_decode(case, kp, vp)
     assert_close(out_f64(a), ref, "bf16", "single pass")
-    assert_close(out_f64(b), ref, "bf16", "one partition")
-    assert_close(out_f64(a), out_f64(b), "bf16", "single pass vs one partition")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "workgroup item != single pass"
+    assert_close(out_f64(c), ref, "bf16", "one partition, wave item")
+    assert_close(out_f64(a), out_f64(c), "bf16", "single pass vs one partition")
+
+
+@pytest.mark.parametrize("dtype,G,D", [("bf16", 4, 128), ("f16", 1, 128), ("f32", 8, 64)])
+def test_splitkv_item_modes_agree_with_oracle(dtype, G, D):
+    """The same inputs through both plans: workgroup items (max_context_len = the longest
+    sequence, 4 partitions of 512) and wave items (max_context_len raised to 20 partitions).
+    Lengths straddle partition edges, include 0 and 1, and sequences with one partition (written
+    directly) sit beside ones that go through the merge."""
+    lens = [0, 1, 15, 16, 17, 511, 512, 513, 1024, 1025, 2000, 1536, 300, 47]
+    case = W.make_decode("modes", dtype, lens, G * 2, 2, D, seed=57 + G)
+    say(f"case: splitkv item modes {dtype} G={G} D={D}")
+    d = DeviceDecode(case)
+    d.scatter()
+    grp = d.decode(split=512, out=torch.full_like(d.q, float("nan"))).clone()
+    wav = d.decode(split=512, out=torch.full_like(d.q, float("nan")), mcl=20 * 512)
+    one = d.decode()
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    ref = oracle_decode(case, kp, vp)
+    assert_close(out_f64(grp), ref, dtype, "workgroup items")
+    assert_close(out_f64(wav), ref, dtype, "wave items")
+    assert not out_f64(grp)[0].any() and not out_f64(wav)[0].any()
+    short = [i for i, L in enumerate(lens) if 0 < L <= 512]
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(grp[short].view(bits), one[short].view(bits)), "one-partition rows != single pass"
+
+
+def test_llama3_gqa_full_size_workgroup_items():
+    """The GQA batch at full size (256 sequences, a shared 512-token prefix for half of them) in
+    512-token partitions (8 partitions planned): the persistent workgroups take many items each.
+    Sequences up to 512 tokens are written directly and equal the single pass bit for bit; a
+    sample of the longer ones, including the longest, is checked against the oracle."""
+    case = W.llama3_8b_gqa_bf16()
+    say(f"case: llama3 GQA split-KV workgroup items, max len {case.max_context_len}")
+    d = DeviceDecode(case)
+    d.scatter()
+    grp = d.decode(split=512, out=torch.full_like(d.q, float("nan"))).clone()
+    one = d.decode()
+    torch.cuda.synchronize()
+    lens = case.context_lens
+    short = torch.from_numpy(np.nonzero((lens > 0) & (lens <= 512))[0]).cuda()
+    assert short.numel() > 0
+    assert torch.equal(grp[short].view(torch.int16), one[short].view(torch.int16))
+    assert not torch.isnan(grp).any()
+    order = np.argsort(lens)
+    seqs = sorted({int(order[-1]), int(order[-2]), int(order[len(order) // 2 + 10]), int(order[-40])})
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    del d
+    assert_close(out_f64(grp)[seqs], oracle_decode(case, kp, vp, seqs), "bf16", "GQA split-KV, sampled")
 
 
 def test_splitkv_rerun_and_block_relabelling_bit_identical():
