@@ -159,7 +159,11 @@ PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_
  *
  * Arguments as pa_decode, plus
  *   max_context_len  upper bound of context_lens (host-known); sequences
- *                    longer than this are a precondition violation
+ *                    longer than this are a precondition violation: such a
+ *                    sequence is cut after ceil(max_context_len /
+ *                    partition_size) partitions (attention over its first
+ *                    that many times partition_size tokens), and nothing is
+ *                    written outside the workspace
  *   partition_size   tokens per partition, a positive multiple of 16
  *   workspace        device buffer of at least
  *                    pa_decode_splitkv_workspace_bytes(...) bytes, 16-byte

@@ -247,6 +247,36 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
   return s_pick;
 }
 
+// Partitions of a sequence of L tokens, at most max_parts: a sequence longer
+// than the max_context_len the call was planned for (a precondition
+// violation) is cut there rather than written past the workspace.
+__device__ __forceinline__ int parts_of(const DecodeParams& p, int L) {
+  const int nb = min((max(L, 0) + kBlockSize - 1) / kBlockSize, p.block_table_stride);
+  return min((nb + p.partition_blocks - 1) / p.partition_blocks, p.max_parts);
+}
+
+// 64 lanes turn v[0..n) into its exclusive prefix sums in place, v[n] = total.
+__device__ __forceinline__ void wave_exclusive_scan(int* v, int n) {
+  const int l = threadIdx.x & 63;
+  const int per = (n + 63) / 64;
+  const int t0 = min(l * per, n), t1 = min(t0 + per, n);
+  int run = 0;
+  for (int t = t0; t < t1; ++t) run += v[t];
+  int inc = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (l >= o) inc += y;
+  }
+  int acc = inc - run;
+  for (int t = t0; t < t1; ++t) {
+    const int c = v[t];
+    v[t] = acc;
+    acc += c;
+  }
+  if (l == 63) v[n] = inc;
+}
+
 // Split-KV work assignment. A work item is one (kv head, sequence, partition)
 // triple that exists. Workgroups start in grid order, and the compute units
 // of the chip do not all finish their share at the same rate (each XCD takes
@@ -269,33 +299,10 @@ __device__ __forceinline__ bool split_work(const DecodeParams& p, int wave, int&
   const bool dense = B <= kRankMaxSeqs;
   if (threadIdx.x == 0) s_ticket = atomicAdd(p.ws_ctr, NT / 64);
   if (dense) {
-    for (int t = threadIdx.x; t < B; t += NT) {
-      const int L = max(p.context_lens[t], 0);
-      const int nb = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-      s_pre[t] = (nb + p.partition_blocks - 1) / p.partition_blocks;
-    }
+    for (int t = threadIdx.x; t < B; t += NT) s_pre[t] = parts_of(p, p.context_lens[t]);
   }
   __syncthreads();
-  if (dense && threadIdx.x < 64) {          // exclusive scan, a run of sequences per lane
-    const int l = threadIdx.x;
-    const int per = (B + 63) / 64;
-    const int t0 = min(l * per, B), t1 = min(t0 + per, B);
-    int run = 0;
-    for (int t = t0; t < t1; ++t) run += s_pre[t];
-    int inc = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (l >= o) inc += y;
-    }
-    int acc = inc - run;
-    for (int t = t0; t < t1; ++t) {
-      const int c = s_pre[t];
-      s_pre[t] = acc;
-      acc += c;
-    }
-    if (l == 63) s_pre[B] = inc;
-  }
+  if (dense && threadIdx.x < 64) wave_exclusive_scan(s_pre, B);   // a run of sequences per lane
   __syncthreads();
   // LDS reads at uniform addresses, made visibly uniform so that the search,
   // the exit and everything derived from (g, b, part) stay scalar
@@ -344,33 +351,6 @@ constexpr int kPlanPre = 2 * kBuckets;                   // bucket members, then
 constexpr int kPlanPerm = kPlanPre + kRankMaxSeqs + 1;   // perm[rank] = sequence
 constexpr int kPlanTicket = kPlanPerm + kRankMaxSeqs;
 constexpr int kPlanInts = kPlanTicket + 1;
-
-__device__ __forceinline__ int parts_of(const DecodeParams& p, int L) {
-  const int nb = min((max(L, 0) + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-  return (nb + p.partition_blocks - 1) / p.partition_blocks;
-}
-
-// 64 lanes turn v[0..n) into its exclusive prefix sums in place, v[n] = total.
-__device__ __forceinline__ void wave_exclusive_scan(int* v, int n) {
-  const int l = threadIdx.x & 63;
-  const int per = (n + 63) / 64;
-  const int t0 = min(l * per, n), t1 = min(t0 + per, n);
-  int run = 0;
-  for (int t = t0; t < t1; ++t) run += v[t];
-  int inc = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (l >= o) inc += y;
-  }
-  int acc = inc - run;
-  for (int t = t0; t < t1; ++t) {
-    const int c = v[t];
-    v[t] = acc;
-    acc += c;
-  }
-  if (l == 63) v[n] = inc;
-}
 
 template <int NT>
 __device__ __forceinline__ void group_plan(const DecodeParams& p, int* s) {

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_463_amd as P
 import workloads as W
 from gpu_cases import DeviceDecode, assert_close, assert_scatter_exact, oracle_decode, out_f64, say, i32
@@ -175,3 +176,30 @@ def test_long_context_bf16_full_size_sampled():
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     del d
     assert_close(out_f64(out)[seqs], oracle_decode(case, kp, vp, seqs), "bf16", "long-context split-KV")
+
+
+@pytest.mark.parametrize("part", [512, 32])        # 2 partitions planned: workgroup items; 32: wave items
+def test_sequence_longer_than_planned_stays_inside_the_workspace(part):
+    """max_context_len is a bound the caller promises; a sequence beyond it (a precondition
+    violation) is cut at the planned partitions instead of being written past the workspace.
+    The workspace is followed by a guard region that must come back untouched, the sequences
+    within the bound are right, and the long one equals attention over its first
+    max_context_len tokens."""
+    lens = [700, 100, 2000, 513]
+    case = W.make_decode("overlong", "bf16", lens, 8, 2, 128, seed=77)
+    d = DeviceDecode(case)
+    d.scatter()
+    mcl = 1024
+    need = P.splitkv_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, mcl, part)
+    guard = 1 << 20
+    ws = torch.full((need + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    say(f"case: sequence of 2000 tokens planned for {mcl}, part={part}")
+    out = d.decode(split=part, workspace=ws, mcl=mcl)
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0x5A).all()), "written past the workspace"
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    got = out_f64(out)
+    assert_close(got[[0, 1, 3]], oracle_decode(case, kp, vp, [0, 1, 3]), "bf16", "sequences within the bound")
+    cut = oracle.paged_decode(case.query[[2]], kp, vp, case.block_tables[[2]], np.array([mcl], dtype=np.int32),
+                              case.scale, case.num_kv_heads, case.dtype)
+    assert_close(got[[2]], cut, "bf16", "long sequence cut at max_context_len")

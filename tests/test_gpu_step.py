@@ -110,10 +110,12 @@ def test_step_graph_replays_a_growing_batch():
     graph.close()
 
 
-def test_step_graph_of_splitkv_and_fp8_step():
+@pytest.mark.parametrize("plan", ["group", "wave"])
+def test_step_graph_of_splitkv_and_fp8_step(plan):
     """A graph holding a split-KV decode (its counter reset is a kernel, not a memset) and
     an FP8 fused step, replayed three times with eager work between; every replay equals
-    the eager calls bit for bit."""
+    the eager calls bit for bit. max_context_len = the longest sequence plans 6 partitions of
+    512 (workgroup items); 20 partitions' worth plans wave items."""
     case = W.make_decode("gsplit", "bf16", [100, 1500, 3000, 17], 16, 2, 128, seed=160)
     d = DeviceDecode(case)
     d.scatter()
@@ -121,10 +123,10 @@ def test_step_graph_of_splitkv_and_fp8_step():
     kp8, vp8 = torch.from_numpy(f.k_pool).cuda(), torch.from_numpy(f.v_pool).cuda()
     kp8_e, vp8_e = kp8.clone(), vp8.clone()
     ks, vs = torch.from_numpy(f.k_scale).cuda(), torch.from_numpy(f.v_scale).cuda()
-    mcl = case.max_context_len
+    mcl = case.max_context_len if plan == "group" else 20 * 512
     ws = torch.empty(P.splitkv_workspace_bytes(case.num_seqs, 16, 128, mcl, 512), dtype=torch.uint8, device="cuda")
     o_split, o_fp8 = torch.empty_like(d.out), torch.empty_like(d.out)
-    say("case: step graph of split-KV + fp8 step, 3 replays")
+    say(f"case: step graph of split-KV ({plan} items) + fp8 step, 3 replays")
     with P.StepGraph() as graph:
         P.decode_splitkv(o_split, d.q, d.kp, d.vp, d.bt, d.lens, case.scale, mcl, 512, ws, stream=graph.stream)
         P.decode_step_fp8(o_fp8, d.q, d.kn, d.vn, kp8, vp8, d.bt, d.lens, case.scale, ks, vs, stream=graph.stream)
