@@ -430,7 +430,11 @@ PA_API int32_t pa_bm_num_cached(const pa_block_manager* m);
  *   seq_lens         int32 [num_seqs], keys in cache INCLUDING the chunk
  *   causal           0 or 1
  *   dtype            PA_DTYPE_BF16 or PA_DTYPE_F16
- * Preconditions beyond the common ones: 0 <= q_len_b <= min(max_q_len, seq_lens[b]).
+ * Preconditions beyond the common ones: 0 <= q_len_b <= min(max_q_len, seq_lens[b]),
+ * cu_q_lens non-decreasing with cu_q_lens[num_seqs] <= num_q_tokens. A call that
+ * violates them still touches only rows [0, num_q_tokens) (offsets are clamped
+ * to it, a chunk longer than seq_lens[b] is cut to that length); the values of
+ * the affected rows are then unspecified.
  */
 PA_API int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_lens,
                            int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,

@@ -136,9 +136,13 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   if (pair >= npairs) return;
   const int b = pair / p.num_kv_heads;
   const int g = pair % p.num_kv_heads;
-  const int cu0 = p.cu_q_lens[b];
-  const int qlen = p.cu_q_lens[b + 1] - cu0;
+  // chunk rows stay inside [0, num_q_tokens) and a chunk never claims more
+  // positions than the sequence has keys: both are preconditions, the clamps
+  // only keep a violating call inside its buffers
+  const int64_t nq = p.num_q_tokens;
   const int L = p.seq_lens[b];
+  const int cu0 = (int)min((int64_t)max(p.cu_q_lens[b], 0), nq);
+  const int qlen = min((int)min((int64_t)max(p.cu_q_lens[b + 1], cu0), nq) - cu0, max(L, 0));
   const int q0 = tile * BQ;                  // first chunk position of this workgroup
   if (q0 >= qlen || L <= 0) return;
   const int s0 = L - qlen;                   // absolute position of chunk position 0

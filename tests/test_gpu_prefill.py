@@ -118,3 +118,27 @@ def test_prefill_rejects_fp32():
     with pytest.raises(P.PagedAttentionError) as e:
         d.run()
     assert e.value.status == 2
+
+
+def test_chunk_offsets_past_the_query_rows_stay_in_bounds():
+    """cu_q_lens promises rows up to 214 but the call passes 180 query rows (a precondition
+    violation): the kernel reads and writes only rows below 180. The query and the output are
+    views into larger buffers whose rows past 180 are a guard that must come back untouched,
+    and the two sequences whose chunks lie inside the rows are still right."""
+    case = W.make_prefill("overrows", "bf16", [40, 200, 90], [64, 100, 50], 8, 2, 128, seed=91)
+    assert case.cu_q_lens.tolist() == [0, 64, 164, 214]
+    d = DevicePrefill(case)
+    P.reshape_and_cache(d.kn, d.vn, d.kp, d.vp, d.slots)
+    rows = 180
+    qbig = torch.full((240,) + tuple(d.q.shape[1:]), 7.0, dtype=d.q.dtype, device="cuda")
+    qbig[:rows] = d.q[:rows]
+    obig = torch.full_like(qbig, float("nan"))
+    say("case: prefill with cu_q_lens past the query rows (180 of 214)")
+    P.prefill_chunked(obig[:rows], qbig[:rows], d.cu, case.max_q_len, d.kp, d.vp, d.bt, d.lens, case.scale, True)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(obig[rows:]).all()), "written past the output rows"
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    ref = oracle.paged_prefill(case.query, kp, vp, case.block_tables, case.seq_lens, case.cu_q_lens,
+                               case.scale, case.num_kv_heads, case.dtype, causal=True, seqs=[0, 1])
+    assert_close(out_f64(obig[:164]), ref[:164], "bf16", "chunks inside the rows")
+    assert not bool(torch.isnan(obig[164:rows]).any())
