@@ -38,11 +38,15 @@
 //   * Block ids are wave-uniform (scalar loads, read a step ahead); two register
 //     buffers keep the next block's K/V loads in flight while a block is computed.
 //
-// Split-KV: every wave covers one (kv head, sequence, partition p) item,
-// logical tokens [partition_size*p, partition_size*(p+1)), on its own, and
-// writes, per query head, the unnormalised output row plus (max, normaliser)
-// to the workspace; a second kernel merges partitions by log-sum-exp. Items
-// are handed out by a work counter (see split_work).
+// Split-KV: a (kv head, sequence, partition p) item covers logical tokens
+// [partition_size*p, partition_size*(p+1)) and writes, per query head, the
+// unnormalised output row plus (max, normaliser) to the workspace; a second
+// kernel merges partitions by log-sum-exp. Two plans, chosen by the number of
+// partitions a sequence can have: above 16, every wave walks one item on its
+// own (wave items, see split_work); up to 16, a workgroup walks one item with
+// its waves taking the blocks round-robin and a one-partition sequence is
+// written directly (workgroup items, see group_work). Items are handed out by
+// a work counter in both.
 #include <math.h>
 
 #include <algorithm>
