@@ -29,7 +29,7 @@ import math
 
 import numpy as np
 
-from .paged_attention import BLOCK_SIZE, attend, gather, kv_head_of, scatter, to_f64, _scale64
+from .paged_attention import BLOCK_SIZE, attend, gather, kv_head_of, scatter, to_f64, visible_keys, _scale64
 
 E4M3_MAX = 448.0
 _MIN_NORMAL_EXP = -6          # 2^-6, exponent field 1
@@ -130,4 +130,35 @@ def paged_decode_fp8(query, k_pool, v_pool, block_tables, context_lens, scale, k
         for h in range(Hq):
             g = kv_head_of(h, Hq, num_kv_heads)
             out[b, h] = attend(q64[b, h], K[:, g], V[:, g], sc)
+    return out
+
+
+def paged_prefill_fp8(query, k_pool, v_pool, block_tables, seq_lens, cu_q_lens, scale, k_scale, v_scale,
+                      num_kv_heads, dtype, causal: bool = True, block_size: int = BLOCK_SIZE,
+                      seqs=None, heads=None) -> np.ndarray:
+    """Chunked prefill over the dequantised cache: the queries of ``paged_attention.paged_prefill``
+    (row ranges from ``cu_q_lens``, causal positions ``seq_lens[b] - q_len + i``) attend over
+    ``K = value(code) * k_scale[h]`` and ``V = value(code) * v_scale[h]`` gathered through the
+    table. ``query`` in ``dtype`` storage; returns float64 ``[T, H_q, D]``, rows outside
+    ``seqs``/``heads`` zero."""
+    T, Hq, D = query.shape
+    sc = _scale64(scale)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    seqs = range(len(seq_lens)) if seqs is None else seqs
+    heads = range(Hq) if heads is None else heads
+    for b in seqs:
+        q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        qlen, L = q1 - q0, int(seq_lens[b])
+        if qlen == 0 or L == 0:
+            continue
+        K = dequantize(gather(k_pool, block_tables[b], L, block_size), k_scale)    # [L, H_kv, D]
+        V = dequantize(gather(v_pool, block_tables[b], L, block_size), v_scale)
+        Q = to_f64(query[q0:q1], dtype)
+        visible = visible_keys(L, qlen, causal)
+        for h in heads:
+            g = kv_head_of(h, Hq, num_kv_heads)
+            S = sc * (Q[:, h] @ K[:, g].T)
+            S = np.where(visible, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            out[q0:q1, h] = (P @ V[:, g]) / P.sum(axis=1, keepdims=True)
     return out

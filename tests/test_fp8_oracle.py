@@ -132,6 +132,39 @@ def test_one_token_context_returns_the_dequantised_value_row():
             assert np.array_equal(got[b, h], t[vc[tables[b, 0], 0, g]] * vs[g])
 
 
+def _prefill_exact_case(rng):
+    """Two sequences over FP8 pools whose dequantised values are exact in f32: 30 cached + 9
+    new tokens and 0 cached + 21 new tokens, 8 query heads over 2 kv heads, head_dim 8."""
+    q, kc, vc, ks, vs, tables, _ = exact_case(rng)
+    seq_lens = np.array([39, 21], np.int32)
+    cu = np.array([0, 9, 30], np.int32)
+    query = rng.standard_normal((30, 8, kc.shape[-1])).astype(np.float32)
+    return query, kc, vc, ks, vs, tables[:2], seq_lens, cu
+
+
+def test_fp8_prefill_equals_prefill_of_the_dequantised_cache():
+    rng = np.random.default_rng(11)
+    query, kc, vc, ks, vs, tables, seq_lens, cu = _prefill_exact_case(rng)
+    t = F.e4m3_table()
+    kf = (t[kc] * ks[None, None, :, None]).astype(np.float32)
+    vf = (t[vc] * vs[None, None, :, None]).astype(np.float32)
+    for causal in (True, False):
+        ref = oracle.paged_prefill(query, kf, vf, tables, seq_lens, cu, 0.3, 2, "f32", causal=causal)
+        got = F.paged_prefill_fp8(query, kc, vc, tables, seq_lens, cu, 0.3, ks, vs, 2, "f32", causal=causal)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+
+
+def test_fp8_prefill_last_chunk_row_equals_fp8_decode():
+    """The last query of a chunk sits at position seq_len - 1 and sees every key: the decode
+    of the same sequence over the same FP8 cache."""
+    rng = np.random.default_rng(12)
+    query, kc, vc, ks, vs, tables, seq_lens, cu = _prefill_exact_case(rng)
+    got = F.paged_prefill_fp8(query, kc, vc, tables, seq_lens, cu, 0.3, ks, vs, 2, "f32")
+    last = query[cu[1:] - 1]
+    dec = F.paged_decode_fp8(last, kc, vc, tables, seq_lens, 0.3, ks, vs, 2, "f32")
+    np.testing.assert_allclose(got[cu[1:] - 1], dec, rtol=0, atol=1e-13)
+
+
 def test_scatter_fp8_writes_codes_at_slots():
     key = np.array([[[1.0, -2.0]], [[448.0, 1000.0]]], np.float32)       # [T=2, H_kv=1, D=2]
     value = -key
@@ -175,3 +208,20 @@ def test_mutation_no_saturation_is_caught(monkeypatch):
     monkeypatch.setattr(F, "e4m3_code", lambda y: 0x7F if abs(y) > 464 and not math.isnan(y) else orig(y))
     with pytest.raises(AssertionError):
         test_encode_saturates_and_keeps_nan_and_signed_zero()
+
+
+def test_mutation_prefill_scales_of_swapped_heads_are_caught(monkeypatch):
+    orig = F.dequantize
+    monkeypatch.setattr(F, "dequantize", lambda pool, scale: orig(pool, np.asarray(scale)[::-1]))
+    with pytest.raises(AssertionError):
+        test_fp8_prefill_equals_prefill_of_the_dequantised_cache()
+
+
+def test_mutation_prefill_k_and_v_scales_exchanged_are_caught(monkeypatch):
+    orig = F.paged_prefill_fp8
+
+    def swapped(query, kp, vp, bt, sl, cu, scale, ks, vs, *a, **kw):
+        return orig(query, kp, vp, bt, sl, cu, scale, vs, ks, *a, **kw)
+    monkeypatch.setattr(F, "paged_prefill_fp8", swapped)
+    with pytest.raises(AssertionError):
+        test_fp8_prefill_equals_prefill_of_the_dequantised_cache()
