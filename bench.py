@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "decode_fp8": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "splitkv_fp8": ["decode.hip", "pa_device.h", "pa_launch.h"],
     "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h"],
+    "prefill_fp8": ["prefill.hip", "pa_device.h", "pa_launch.h"],
     "copy_blocks": ["block_copy.hip", "pa_device.h", "pa_launch.h"],
 }
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
@@ -56,6 +57,7 @@ WORKLOADS = {
     "llama2_7b_fp8kv_decode_b64": ("llama2_7b_fp16", "decode_fp8"),
     "llama3_8b_gqa_fp8kv_decode_b256": ("llama3_8b_gqa_bf16", "decode_fp8"),
     "long_ctx_fp8kv_splitkv_b8": ("long_context_bf16", "splitkv_fp8"),
+    "chunked_prefill_fp8kv_16x2048p512": ("chunked_prefill_bf16", "prefill_fp8"),
 }
 DEFAULT_WORKLOAD = "llama2_7b_fp16_decode_b64"
 # block movement: name -> (pool blocks, kv heads, head_dim, copy pairs, swap blocks)
@@ -175,7 +177,7 @@ class Runner:
         self.bt = i32(case.block_tables)
         self.out = torch.empty_like(self.q)
         self.layers = layers
-        if call == "prefill":
+        if call.startswith("prefill"):
             self.cu = i32(case.cu_q_lens)
             self.lens = i32(case.seq_lens)
             self.max_q = case.max_q_len
@@ -239,6 +241,9 @@ class Runner:
         elif self.call == "splitkv_fp8":
             P.decode_splitkv_fp8(self.out, self.q, self.kp[layer], self.vp[layer], self.bt, self.lens, c.scale,
                                  self.ks, self.vs, self.mcl, self.partition, self.ws)
+        elif self.call == "prefill_fp8":
+            P.prefill_chunked_fp8(self.out, self.q, self.cu, self.max_q, self.kp[layer], self.vp[layer], self.bt,
+                                  self.lens, c.scale, self.ks, self.vs, True)
         else:
             P.prefill_chunked(self.out, self.q, self.cu, self.max_q, self.kp[layer], self.vp[layer], self.bt,
                               self.lens, c.scale, True)
@@ -331,10 +336,16 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
     while True:                                 # whole passes over the batch until the budget is spent
         for b in order:
             b = int(b)
-            if call == "prefill":
+            if call.startswith("prefill"):
                 heads = list(range(case.num_q_heads))
-                ref = oracle.paged_prefill(case.query, kp, vp, case.block_tables, case.seq_lens, case.cu_q_lens,
-                                           case.scale, case.num_kv_heads, case.dtype, seqs=[b], heads=heads)
+                if r.fp8:
+                    ref = oracle.fp8.paged_prefill_fp8(case.query, kp, vp, case.block_tables, case.seq_lens,
+                                                       case.cu_q_lens, case.scale, f.k_scale, f.v_scale,
+                                                       case.num_kv_heads, case.dtype, seqs=[b], heads=heads)
+                else:
+                    ref = oracle.paged_prefill(case.query, kp, vp, case.block_tables, case.seq_lens,
+                                               case.cu_q_lens, case.scale, case.num_kv_heads, case.dtype,
+                                               seqs=[b], heads=heads)
                 q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
                 err = max(err, float(np.abs(ref[q0:q1] - gpu_out[q0:q1]).max()))
                 units += q1 - q0
@@ -357,7 +368,7 @@ def cpu_baseline(case, call: str, r: Runner, budget_s: float):
             continue
         break
     secs = time.perf_counter() - t0
-    unit = "query-tokens/s" if call == "prefill" else "seq-steps/s"
+    unit = "query-tokens/s" if call.startswith("prefill") else "seq-steps/s"
     return {"value": units / secs, "unit": unit, "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} sequence-steps ({passes} whole passes over the {case.num_seqs}-sequence batch "
                       f"plus {len(done) - passes * case.num_seqs} sequences), all heads, fp64 NumPy, {secs:.1f} s",
@@ -463,7 +474,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--kernel", default=None,
-                    choices=["decode", "splitkv", "prefill", "decode_fp8", "splitkv_fp8"],
+                    choices=["decode", "splitkv", "prefill", "decode_fp8", "splitkv_fp8", "prefill_fp8"],
                     help="attention entry point (default: the workload's)")
     ap.add_argument("--partition", type=int, default=512, help="split-KV partition size (tokens)")
     ap.add_argument("--layers", type=int, default=4, help="KV pool replicas rotated over steps")
@@ -513,7 +524,7 @@ def main(argv=None) -> int:
            "num_seqs": case.num_seqs,
            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
            "kv_pool_replicas": args.layers}
-    if call == "prefill":
+    if call.startswith("prefill"):
         flops = prefill_flops(case)
         tokens = case.num_q_tokens
         res.update({"value": tokens * args.steps / elapsed, "unit": "query-tokens/s"})

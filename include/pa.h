@@ -444,6 +444,24 @@ PA_API int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* c
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            float scale, int32_t causal, int32_t dtype, void* stream);
 
+/*
+ * pa_prefill_chunked_fp8 — pa_prefill_chunked over an FP8 (e4m3) cache written
+ * by pa_reshape_and_cache_fp8: the same chunked attention over the dequantised
+ * keys and values, value(code) * k_scale[h] and value(code) * v_scale[h] (the
+ * FP8 reading of pa_decode_fp8). Queries and outputs are f16 or bf16; the
+ * pools hold one byte per element and block_stride counts bytes; k_scale and
+ * v_scale are float32 [num_kv_heads] device arrays (NULL: PA_ERR_NULL_PTR).
+ * Other arguments, preconditions and errors as pa_prefill_chunked.
+ */
+PA_API int32_t pa_prefill_chunked_fp8(void* out, const void* query, const int32_t* cu_q_lens,
+                               int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                               const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               float scale, int32_t causal, const float* k_scale, const float* v_scale,
+                               int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     decode_splitkv_fp8,
     lib,
     prefill_chunked,
+    prefill_chunked_fp8,
     reshape_and_cache,
     reshape_and_cache_fp8,
     splitkv_workspace_bytes,
@@ -29,5 +30,5 @@ from ._binding import (  # noqa: F401
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
            "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8", "decode_step", "decode_step_fp8",
            "StepGraph",
-           "prefill_chunked", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
+           "prefill_chunked", "prefill_chunked_fp8", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
            "LibraryNotBuilt", "PagedAttentionError"]

@@ -37,6 +37,8 @@ SIGNATURES = {
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
+    "pa_prefill_chunked_fp8": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
+                                      _i32, _i32, _i32, _f32, _i32, _p, _p, _i32, _p]),
     "pa_decode_step": (_i32, [_p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                _i32, _f32, _i32, _p]),
     "pa_decode_step_fp8": (_i32, [_p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32,
@@ -355,6 +357,23 @@ def prefill_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Ten
         _ptr(out), _ptr(query), _ptr(cu_q_lens), max_q_len, T, _ptr(k_cache), _ptr(v_cache), bstride,
         nb, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), seq_lens.numel(), hq, hkv, d,
         bs, scale, int(bool(causal)), _dtype(query), _stream(stream)))
+
+
+def prefill_chunked_fp8(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                        seq_lens: torch.Tensor, scale: float, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                        causal: bool = True, stream=None) -> None:
+    """Chunked (causal) prefill over FP8 pools; ``out``/``query`` ``[T, H_q, D]`` in f16 or bf16."""
+    nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
+    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
+    _i32_tensor(cu_q_lens, "cu_q_lens")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(seq_lens, "seq_lens")
+    T, hq, _ = query.shape
+    _check("pa_prefill_chunked_fp8", lib().pa_prefill_chunked_fp8(
+        _ptr(out), _ptr(query), _ptr(cu_q_lens), max_q_len, T, _ptr(k_cache), _ptr(v_cache), bstride,
+        nb, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), seq_lens.numel(), hq, hkv, d,
+        bs, scale, int(bool(causal)), _ptr(k_scale), _ptr(v_scale), _dtype(query), _stream(stream)))
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, stream=None) -> None:

@@ -443,23 +443,29 @@ int32_t pa_decode_splitkv_fp8(void* out, const void* query, const void* k_cache,
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 
-int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_lens,
-                           int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
-                           const void* v_cache, int64_t block_stride, int64_t num_blocks,
-                           const int32_t* block_tables, int32_t block_table_stride,
-                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                           float scale, int32_t causal, int32_t dtype, void* stream) {
+// Shared argument checks and parameter block of the two prefill entry points;
+// cache_bytes = 0: the cache has the query's type, 1: FP8 codes.
+static int32_t prefill_params(pa::PrefillParams& p, void* out, const void* query, const int32_t* cu_q_lens,
+                              int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                              const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                              int32_t causal, int32_t dtype, int cache_bytes, bool& empty) {
+  empty = false;
   int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
                                       block_tables, block_table_stride, seq_lens, num_seqs,
-                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype, cache_bytes);
   if (st != PA_OK) return st;
   if (dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16) return PA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
   if (max_q_len < 0 || num_q_tokens < 0) return PA_ERR_SHAPE;
-  if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) {
+    empty = true;
+    return PA_OK;
+  }
   if (!cu_q_lens) return PA_ERR_NULL_PTR;
-  pa::PrefillParams p{};
+  p = pa::PrefillParams{};
   p.out = out;
   p.query = query;
   p.cu_q_lens = cu_q_lens;
@@ -467,7 +473,7 @@ int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_len
   p.num_q_tokens = num_q_tokens;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
-  p.block_stride_bytes = block_stride * elem_bytes(dtype);
+  p.block_stride_bytes = block_stride * (cache_bytes ? cache_bytes : elem_bytes(dtype));
   p.num_blocks = num_blocks;
   p.block_tables = block_tables;
   p.block_table_stride = block_table_stride;
@@ -479,7 +485,45 @@ int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_len
   p.dtype = dtype;
   p.causal = causal;
   p.scale = scale;
+  return PA_OK;
+}
+
+int32_t pa_prefill_chunked(void* out, const void* query, const int32_t* cu_q_lens,
+                           int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                           const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                           const int32_t* block_tables, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t causal, int32_t dtype, void* stream) {
+  pa::PrefillParams p;
+  bool empty;
+  const int32_t st = prefill_params(p, out, query, cu_q_lens, max_q_len, num_q_tokens, k_cache, v_cache,
+                                    block_stride, num_blocks, block_tables, block_table_stride, seq_lens,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale, causal,
+                                    dtype, 0, empty);
+  if (st != PA_OK || empty) return st;
   hipError_t e = pa::launch_prefill(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int32_t pa_prefill_chunked_fp8(void* out, const void* query, const int32_t* cu_q_lens,
+                               int32_t max_q_len, int64_t num_q_tokens, const void* k_cache,
+                               const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               float scale, int32_t causal, const float* k_scale, const float* v_scale,
+                               int32_t dtype, void* stream) {
+  pa::PrefillParams p;
+  bool empty;
+  const int32_t st = prefill_params(p, out, query, cu_q_lens, max_q_len, num_q_tokens, k_cache, v_cache,
+                                    block_stride, num_blocks, block_tables, block_table_stride, seq_lens,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale, causal,
+                                    dtype, 1, empty);
+  if (st != PA_OK || empty) return st;
+  if (!k_scale || !v_scale) return PA_ERR_NULL_PTR;
+  hipError_t e = pa::launch_prefill_fp8(p, k_scale, v_scale, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
   return hip_status(e);
 }

@@ -109,5 +109,7 @@ hipError_t launch_swap_chunk(const SwapChunk& c, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// chunked prefill over an FP8 (e4m3) cache: per-kv-head dequantisation scales
+hipError_t launch_prefill_fp8(const PrefillParams& p, const float* k_scale, const float* v_scale, hipStream_t s);
 
 }  // namespace pa

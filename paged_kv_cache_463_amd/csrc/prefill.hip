@@ -98,9 +98,16 @@ __device__ __forceinline__ V as_vec(const u32x4& u) { return __builtin_bit_cast(
 
 }  // namespace
 
-template <DT dt, int D, int G>
+// F8: K and V come from an FP8 (e4m3) cache. Each wave then loads its block of
+// the tile into registers with ordinary 16-byte loads (issued where the 16-bit
+// path issues its direct global->LDS loads), widens the codes to the query
+// type (exact) when the tile lands, and writes them into LDS in the same
+// swizzled 16-bit layout, so everything after the landing is shared with the
+// 16-bit path. k_scale[g] joins the score scale and v_scale[g] the output.
+template <DT dt, int D, int G, bool F8>
 __global__ __launch_bounds__(64 * kWaves, 2)
-void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
+void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const float* k_scale,
+                    const float* v_scale) {
   using M = Mfma<dt>;
   using vec = typename M::vec;
   constexpr int BQ = kCols / G;              // chunk positions per workgroup
@@ -109,6 +116,8 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   constexpr int MD = D / 32;                 // 32-row tiles of head_dim in O^T
   constexpr int RB = D * 2;                  // bytes of one K/V row in LDS (unpadded, swizzled)
   constexpr int NI = kBlockSize * RB / 1024; // 1 KB DMA instructions per wave per tile (4 or 2)
+  constexpr int NL8 = D / 64;                // FP8: 16-byte loads per lane per block (2 or 1)
+  constexpr int NPARTS = F8 ? 2 * NL8 : 2 * NI;   // load instructions per wave per tile
 
   // K and V tiles, row-major, two buffers each, filled by direct global->LDS
   // loads. 16-byte granule c of row r sits at position c ^ kswz(r) (K) or
@@ -184,7 +193,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
       (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.block_table_stride);
   const char* kc = static_cast<const char*>(p.k_cache);
   const char* vc = static_cast<const char*>(p.v_cache);
-  const int64_t prow = (int64_t)p.num_kv_heads * D * 2;     // bytes of one pool row (all kv heads)
+  const int64_t prow = (int64_t)p.num_kv_heads * D * (F8 ? 1 : 2);   // bytes of one pool row (all kv heads)
   auto kswz = [](int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz = [](int r) { return RB == 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
   uint32_t k_src[NI], v_src[NI];
@@ -196,6 +205,17 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     k_src[n] = row_off + ((gp ^ kswz(r)) << 4);     // the swizzles use the row's low 4 bits only
     v_src[n] = row_off + ((gp ^ vswz(r)) << 4);
   }
+  // FP8: lane l loads row l/4 of the wave's block, bytes (l%4)*D/4 .. +D/4 of
+  // the head's row, as NL8 16-byte loads; load i holds elements e0 .. e0+15,
+  // e0 = (l%4)*D/4 + 16i, which are 16-bit granules e0/8 and e0/8 + 1
+  const int r8 = lane >> 2, q8 = lane & 3;
+  uint32_t f8_src[NL8];
+#pragma unroll
+  for (int i = 0; i < NL8; ++i)
+    f8_src[i] = (uint32_t)(r8 * prow + (int64_t)g * D + q8 * (D / 4) + 16 * i);
+  u32x4 k8[NL8], v8[NL8];                    // FP8: this wave's loads of the tile in flight
+  const uint8_t* pend_kd = nullptr;          // FP8: their LDS destinations
+  const uint8_t* pend_vd = nullptr;
   // table entry of this wave's logical block in tile t (scalar: the index is
   // uniform), and the byte offset of its physical block; blocks past the
   // visible keys read block 0
@@ -228,18 +248,40 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     return {kc + block_base(tk, kbid), vc + block_base(tv, vbid), &sK[kb][wave * kBlockSize * RB],
             &sV[vb][wave * kBlockSize * RB]};
   };
-  auto dma_part = [&](const DmaJob& j, int n) {      // n in [0, 2*NI)
-    if (n < NI) lds_load16(j.ks, k_src[n], j.kd + n * 1024);
-    else lds_load16(j.vs, v_src[n - NI], j.vd + (n - NI) * 1024);
+  auto dma_part = [&](const DmaJob& j, int n) {      // n in [0, NPARTS)
+    if constexpr (F8) {
+      if (n == 0) {
+        pend_kd = j.kd;
+        pend_vd = j.vd;
+      }
+      if (n < NL8) k8[n] = load16(j.ks + f8_src[n]);
+      else v8[n - NL8] = load16(j.vs + f8_src[n - NL8]);
+    } else {
+      if (n < NI) lds_load16(j.ks, k_src[n], j.kd + n * 1024);
+      else lds_load16(j.vs, v_src[n - NI], j.vd + (n - NI) * 1024);
+    }
   };
   auto dma = [&](int tk, int kbid, int kb, int tv, int vbid, int vb) {
     const DmaJob j = dma_job(tk, kbid, kb, tv, vbid, vb);
 #pragma unroll
-    for (int n = 0; n < 2 * NI; ++n) dma_part(j, n);
+    for (int n = 0; n < NPARTS; ++n) dma_part(j, n);
   };
   // wait for this wave's loads; in the last V tile zero the rows of keys past
   // kend (stale slots) in this wave's block, then make everything visible
   auto land = [&](int tv, int vb) {
+    if constexpr (F8) {                      // widen this wave's rows into the 16-bit layout
+#pragma unroll
+      for (int i = 0; i < NL8; ++i) {
+        const int g0 = (q8 * (D / 4) + 16 * i) / 8;
+        const u32x4 kw = k8[i], vw = v8[i];
+        uint8_t* kd = const_cast<uint8_t*>(pend_kd) + r8 * RB;
+        uint8_t* vd = const_cast<uint8_t*>(pend_vd) + r8 * RB;
+        *reinterpret_cast<u32x4*>(kd + ((g0 ^ kswz(r8)) << 4)) = widen_fp8<dt>(u32x2{kw[0], kw[1]});
+        *reinterpret_cast<u32x4*>(kd + (((g0 + 1) ^ kswz(r8)) << 4)) = widen_fp8<dt>(u32x2{kw[2], kw[3]});
+        *reinterpret_cast<u32x4*>(vd + ((g0 ^ vswz(r8)) << 4)) = widen_fp8<dt>(u32x2{vw[0], vw[1]});
+        *reinterpret_cast<u32x4*>(vd + (((g0 + 1) ^ vswz(r8)) << 4)) = widen_fp8<dt>(u32x2{vw[2], vw[3]});
+      }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tv < nkt && tv * kBK + kBK > kend) {
 #pragma unroll
@@ -260,7 +302,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
     for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
   float mref = -INFINITY;
   float lsum = 0.f;
-  const float sl2 = p.scale * kLog2e;
+  const float sl2 = p.scale * kLog2e * (F8 ? k_scale[g] : 1.f);
 
   // Software pipeline over key tiles: iteration t computes the scores of tile
   // t+1 on the matrix cores while the VALU turns the scores of tile t into P,
@@ -370,7 +412,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
         }
         // this tile's global -> LDS loads, spread over the k-steps
 #pragma unroll
-        for (int n = ds * 2 * NI / DS; n < (ds + 1) * 2 * NI / DS; ++n) dma_part(job, n);
+        for (int n = ds * NPARTS / DS; n < (ds + 1) * NPARTS / DS; ++n) dma_part(job, n);
         if (ds == 0) {
           const f32x16 z = {};
           sn[0] = M::run(ka[0][0], qreg[0], z);
@@ -443,7 +485,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   // ---- normalise and store ------------------------------------------------
   const float l = lsum + __shfl_xor(lsum, 32);
   if (!cvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = (l > 0.f ? 1.f / l : 0.f) * (F8 ? v_scale[g] : 1.f);
   uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)(cu0 + qpos) * p.num_q_heads + g * G + hl) * D;
 #pragma unroll
   for (int md = 0; md < MD; ++md) {
@@ -458,8 +500,8 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped) {
   }
 }
 
-template <DT dt, int D>
-static hipError_t launch_dg(const PrefillParams& p, hipStream_t s) {
+template <DT dt, int D, bool F8>
+static hipError_t launch_dg(const PrefillParams& p, const float* ks, const float* vs, hipStream_t s) {
   const int G = p.num_q_heads / p.num_kv_heads;
   const int BQ = kCols / G;
   const int tiles = (p.max_q_len + BQ - 1) / BQ;
@@ -469,25 +511,31 @@ static hipError_t launch_dg(const PrefillParams& p, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   dim3 grid((unsigned)nwg), block(64 * kWaves);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<dt, D, 1>), grid, block, 0, s, p, tiles, xcd); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<dt, D, 2>), grid, block, 0, s, p, tiles, xcd); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<dt, D, 4>), grid, block, 0, s, p, tiles, xcd); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<dt, D, 8>), grid, block, 0, s, p, tiles, xcd); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<dt, D, 1, F8>), grid, block, 0, s, p, tiles, xcd, ks, vs); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<dt, D, 2, F8>), grid, block, 0, s, p, tiles, xcd, ks, vs); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<dt, D, 4, F8>), grid, block, 0, s, p, tiles, xcd, ks, vs); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<dt, D, 8, F8>), grid, block, 0, s, p, tiles, xcd, ks, vs); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+template <bool F8>
+static hipError_t launch_any(const PrefillParams& p, const float* ks, const float* vs, hipStream_t s) {
   const DT dt = static_cast<DT>(p.dtype);
   if (p.head_dim == 128) {
-    if (dt == DT::BF16) return launch_dg<DT::BF16, 128>(p, s);
-    if (dt == DT::F16) return launch_dg<DT::F16, 128>(p, s);
+    if (dt == DT::BF16) return launch_dg<DT::BF16, 128, F8>(p, ks, vs, s);
+    if (dt == DT::F16) return launch_dg<DT::F16, 128, F8>(p, ks, vs, s);
   } else if (p.head_dim == 64) {
-    if (dt == DT::BF16) return launch_dg<DT::BF16, 64>(p, s);
-    if (dt == DT::F16) return launch_dg<DT::F16, 64>(p, s);
+    if (dt == DT::BF16) return launch_dg<DT::BF16, 64, F8>(p, ks, vs, s);
+    if (dt == DT::F16) return launch_dg<DT::F16, 64, F8>(p, ks, vs, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) { return launch_any<false>(p, nullptr, nullptr, s); }
+hipError_t launch_prefill_fp8(const PrefillParams& p, const float* k_scale, const float* v_scale, hipStream_t s) {
+  return launch_any<true>(p, k_scale, v_scale, s);
 }
 
 }  // namespace pa

@@ -117,6 +117,23 @@ def test_prefill_checks():
     assert call(B=0) == OK
 
 
+def test_prefill_fp8_checks():
+    lib = P.lib()
+
+    def call(dtype=2, causal=1, cu=FAKE, T=8192, B=16, ks=FAKE, vs=FAKE, bstride=16 * 8 * 128):
+        return lib.pa_prefill_chunked_fp8(FAKE, FAKE, cu, 512, T, FAKE, FAKE, bstride, 2816, FAKE, 160,
+                                          FAKE, B, 32, 8, 128, 16, 0.088, causal, ks, vs, dtype, None)
+    assert call(dtype=0) == DTYPE                  # fp32 queries are not read with an FP8 cache
+    assert call(dtype=3) == DTYPE
+    assert call(causal=2) == SHAPE
+    assert call(cu=None) == NULL
+    assert call(ks=None) == NULL and call(vs=None) == NULL
+    assert call(bstride=16 * 8 * 128 - 1) == SHAPE  # one byte per element: at least 16 * H_kv * D
+    assert call(bstride=16 * 8 * 128 + 8) == ALIGN
+    assert call(T=0) == OK
+    assert call(B=0) == OK
+
+
 def _scatter_fp8(**kw):
     a = dict(key=FAKE, value=FAKE, ts=8 * 128, k=FAKE, v=FAKE, bstride=16 * 8 * 128, nb=10, slots=FAKE,
              T=5, hkv=8, d=128, bs=16, ks=FAKE, vs=FAKE, dtype=2)

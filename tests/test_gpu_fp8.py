@@ -231,3 +231,93 @@ def test_fp8_long_context_splitkv_full_size_sampled():
     rk, rv = x.check_scatter()
     x.kp = x.vp = None                                       # free the device pools first
     assert_close(out_f64(out)[seqs], x.oracle(rk, rv, seqs), "bf16", "fp8 long-context split-KV")
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over an FP8 cache
+# ---------------------------------------------------------------------------
+class DeviceFp8Prefill:
+    """Device copies of one prefill case with FP8 pools (``workloads.fp8_pools``: random live
+    codes, NaN codes in every slot the 16-bit pools poison)."""
+
+    def __init__(self, case, seed: int = 0):
+        self.case = case
+        self.f = W.fp8_pools(case, seed)
+        self.kp = torch.from_numpy(self.f.k_pool).cuda()
+        self.vp = torch.from_numpy(self.f.v_pool).cuda()
+        self.ks = torch.from_numpy(self.f.k_scale).cuda()
+        self.vs = torch.from_numpy(self.f.v_scale).cuda()
+        self.q = dev(case.query, case.dtype)
+        self.kn, self.vn = dev(case.k_new, case.dtype), dev(case.v_new, case.dtype)
+        self.slots, self.bt = i32(case.slot_mapping), i32(case.block_tables)
+        self.cu, self.lens = i32(case.cu_q_lens), i32(case.seq_lens)
+
+    def run(self, causal=True):
+        out = torch.full_like(self.q, float("nan"))
+        P.reshape_and_cache_fp8(self.kn, self.vn, self.kp, self.vp, self.slots, self.ks, self.vs)
+        P.prefill_chunked_fp8(out, self.q, self.cu, self.case.max_q_len, self.kp, self.vp, self.bt, self.lens,
+                              self.case.scale, self.ks, self.vs, causal)
+        return out
+
+    def oracle(self, causal=True, seqs=None, heads=None):
+        c = self.case
+        rk, rv = F.scatter_fp8(self.f.k_pool, self.f.v_pool, c.k_new, c.v_new, c.slot_mapping,
+                               self.f.k_scale, self.f.v_scale, c.dtype)
+        gk, gv = self.kp.cpu().numpy(), self.vp.cpu().numpy()
+        assert gk.tobytes() == rk.tobytes() and gv.tobytes() == rv.tobytes(), "fp8 scatter differs"
+        return F.paged_prefill_fp8(c.query, rk, rv, c.block_tables, c.seq_lens, c.cu_q_lens, c.scale,
+                                   self.f.k_scale, self.f.v_scale, c.num_kv_heads, c.dtype, causal=causal,
+                                   seqs=seqs, heads=heads)
+
+
+PF_PRIOR = [0, 5, 32, 47, 100, 16]
+PF_QLEN = [9, 16, 1, 37, 300, 0]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_fp8_shapes(dtype, d, G, causal):
+    """Ragged chunks (an empty one, one of a single token, one of 300 over 100 cached tokens)
+    over FP8 pools with NaN codes in dead slots, against the oracle over the dequantised cache."""
+    case = W.make_prefill("fp8pf", dtype, PF_PRIOR, PF_QLEN, G * 2, 2, d, seed=300 + G + d)
+    say(f"case: fp8 prefill {dtype} D={d} G={G} causal={causal}")
+    x = DeviceFp8Prefill(case, seed=G)
+    out = x.run(causal)
+    torch.cuda.synchronize()
+    assert_close(out_f64(out), x.oracle(causal), dtype, f"fp8 prefill D={d} G={G} causal={causal}")
+
+
+def test_prefill_fp8_equals_16bit_prefill_of_the_same_values():
+    """With unit scales every code's value is exact in bf16: a bf16 cache holding those values
+    and the FP8 cache give the MFMAs the same operands, so the two prefills agree bit for bit."""
+    case = W.make_prefill("fp8pfeq", "bf16", [64, 0, 200], [64, 33, 128], 32, 8, 128, seed=311)
+    x = DeviceFp8Prefill(case, seed=7)
+    x.ks.fill_(1.0)
+    x.vs.fill_(1.0)
+    say("case: fp8 prefill vs bf16 prefill of the same values")
+    a = x.run(True)                                         # scatters the chunk, then attends
+    t = F.e4m3_table().astype(np.float32)
+    vals_k = torch.from_numpy(t[x.kp.cpu().numpy()]).to(torch.bfloat16).cuda()
+    vals_v = torch.from_numpy(t[x.vp.cpu().numpy()]).to(torch.bfloat16).cuda()
+    b = torch.full_like(a, float("nan"))
+    P.prefill_chunked(b, x.q, x.cu, case.max_q_len, vals_k, vals_v, x.bt, x.lens, case.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_prefill_fp8_chunked_prefill_shapes_sampled():
+    """The chunked-prefill workload's shapes (16 sequences, 2048 cached + 512 new tokens, 32/8
+    heads, head_dim 128) over an FP8 cache; sampled sequences and heads against the oracle."""
+    case = W.chunked_prefill_bf16()
+    say("case: fp8 prefill at the chunked-prefill workload's shapes, sampled")
+    x = DeviceFp8Prefill(case, seed=13)
+    out = x.run(True)
+    torch.cuda.synchronize()
+    seqs, heads = [0, 9, 15], [0, 5, 31]
+    ref = x.oracle(True, seqs=seqs, heads=heads)
+    rows = np.concatenate([np.arange(case.cu_q_lens[b], case.cu_q_lens[b + 1]) for b in seqs])
+    got = out_f64(out)
+    assert not np.isnan(got).any()
+    assert_close(got[rows][:, heads], ref[rows][:, heads], "bf16", "fp8 prefill, sampled")
