@@ -194,6 +194,10 @@ constexpr uint32_t kOnes2 = dt == DT::BF16 ? 0x3F803F80u : 0x3C003C00u;
 // kRankMaxSeqs sequences keep grid order.
 constexpr int kBuckets = 128;
 constexpr int kRankMaxSeqs = 1024;
+// Up to this many sequences, a thread per sequence counts the larger keys
+// directly (two barriers; the same order, since buckets are monotone in
+// length and keys break ties the same way) — cheaper than the bucket pass.
+constexpr int kRankDirectSeqs = 128;
 
 __device__ __forceinline__ int length_bucket(int L) {
   if (L <= 0) return kBuckets - 1;
@@ -210,6 +214,21 @@ template <int NT>
 __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r) {
   static_assert(NT >= kBuckets / 2, "one scan wave covers the buckets");
   if (B > kRankMaxSeqs) return r;
+  if (B <= kRankDirectSeqs && B <= NT) {     // small batch: count larger keys directly
+    __shared__ int s_k[kRankDirectSeqs];
+    __shared__ int s_pick1;
+    const int t = threadIdx.x;
+    const int key = t < B ? rank_key(lens[t], t) : 0;
+    if (t < B) s_k[t] = key;
+    __syncthreads();
+    if (t < B) {
+      int rank = 0;
+      for (int u = 0; u < B; ++u) rank += s_k[u] > key;   // every lane reads the same word: a broadcast
+      if (rank == r) s_pick1 = t;
+    }
+    __syncthreads();
+    return s_pick1;
+  }
   __shared__ int s_base[kBuckets];
   __shared__ int s_cur[kBuckets];
   __shared__ int s_key[kRankMaxSeqs];
