@@ -211,28 +211,36 @@ __device__ __forceinline__ int rank_key(int L, int t) {          // unique for t
 }
 
 template <int NT>
-__device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r) {
+__device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r, int& len) {
   static_assert(NT >= kBuckets / 2, "one scan wave covers the buckets");
-  if (B > kRankMaxSeqs) return r;
+  if (B > kRankMaxSeqs) {
+    len = lens[r];
+    return r;
+  }
   if (B <= kRankDirectSeqs && B <= NT) {     // small batch: count larger keys directly
     __shared__ int s_k[kRankDirectSeqs];
-    __shared__ int s_pick1;
+    __shared__ int s_pick1, s_len1;
     const int t = threadIdx.x;
-    const int key = t < B ? rank_key(lens[t], t) : 0;
+    const int Lt = t < B ? lens[t] : 0;
+    const int key = rank_key(Lt, t);
     if (t < B) s_k[t] = key;
     __syncthreads();
     if (t < B) {
       int rank = 0;
       for (int u = 0; u < B; ++u) rank += s_k[u] > key;   // every lane reads the same word: a broadcast
-      if (rank == r) s_pick1 = t;
+      if (rank == r) {
+        s_pick1 = t;
+        s_len1 = Lt;                           // the length travels with the pick
+      }
     }
     __syncthreads();
-    return s_pick1;
+    len = __builtin_amdgcn_readfirstlane(s_len1);
+    return __builtin_amdgcn_readfirstlane(s_pick1);
   }
   __shared__ int s_base[kBuckets];
   __shared__ int s_cur[kBuckets];
   __shared__ int s_key[kRankMaxSeqs];
-  __shared__ int s_pick;
+  __shared__ int s_pick, s_len;
   for (int i = threadIdx.x; i < kBuckets; i += NT) s_cur[i] = 0;
   __syncthreads();
   for (int t = threadIdx.x; t < B; t += NT) atomicAdd(&s_cur[length_bucket(lens[t])], 1);
@@ -264,10 +272,14 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
     const int lo = s_base[k], hi = s_cur[k];
     int rank = lo;
     for (int j = lo; j < hi; ++j) rank += s_key[j] > key;
-    if (rank == r) s_pick = t;
+    if (rank == r) {
+      s_pick = t;
+      s_len = L;
+    }
   }
   __syncthreads();
-  return s_pick;
+  len = __builtin_amdgcn_readfirstlane(s_len);
+  return __builtin_amdgcn_readfirstlane(s_pick);
 }
 
 // Partitions of a sequence of L tokens, at most max_parts: a sequence longer
@@ -496,14 +508,14 @@ void decode_kernel(DecodeParams p) {
   if constexpr (GROUP) group_plan<64 * W>(p, s_plan);
   // one trip, except with workgroup items: then one trip per item
   for (;;) {
-  int g, b, part = 0, np = 1;
+  int g, b, part = 0, np = 1, Lb = 0;
   if constexpr (MODE == kWaveItems) {
     if (!split_work<64 * W>(p, wave, g, b, part)) return;   // no work item left
   } else if constexpr (GROUP) {
     if (!group_work<64 * W>(p, s_plan, g, b, part, np)) return;
   } else {
     g = blockIdx.x;
-    b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y);
+    b = sequence_of_row<64 * W>(p.context_lens, p.num_seqs, blockIdx.y, Lb);   // and its length
   }
   const int hq0 = g * G;
 
@@ -514,7 +526,7 @@ void decode_kernel(DecodeParams p) {
   // wave's loads, separates the write from the attention.
   if constexpr (MODE == kSingle) {
     if (p.key_new) {                        // uniform: a kernel argument
-      const int pos = p.context_lens[b] - 1;
+      const int pos = Lb - 1;
       constexpr int NCH = D / 8;            // 8-element chunks of one head's row
       if (pos >= 0 && pos / kBlockSize < p.block_table_stride && threadIdx.x < 2 * NCH) {
         const int bid = p.block_tables[(int64_t)b * p.block_table_stride + pos / kBlockSize];
@@ -544,7 +556,7 @@ void decode_kernel(DecodeParams p) {
     }
   }
 
-  const int L = max(p.context_lens[b], 0);
+  const int L = max(MODE == kSingle ? Lb : p.context_lens[b], 0);
   const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   // single pass and workgroup items: the W waves share the blocks round-robin.
   // wave items: every wave walks one partition on its own (no merge across waves)
