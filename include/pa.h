@@ -211,7 +211,12 @@ PA_API int32_t pa_decode_step(void* out, const void* query, const void* key_new,
  * instantiates them. pa_graph_launch replays the recording on `stream`.
  * Pointers, sizes and grids are frozen at capture; device memory (lengths,
  * tables, K/V, queries) is read at replay, so one graph serves every step of
- * a batch size whose buffers keep their addresses. Recordable calls: those
+ * a batch size whose buffers keep their addresses. A captured split-KV call
+ * also freezes its max_context_len and the plan derived from it (partition
+ * count, workspace layout, workgroup or wave items): capture it with a
+ * max_context_len that bounds the lengths of every later replay, since a
+ * sequence that grows past it is cut at the planned partitions (see
+ * pa_decode_splitkv). Recordable calls: those
  * that only launch kernels (every call except pa_swap_blocks and the pa_bm_*
  * host calls). The graph owns its stream and executable until
  * pa_graph_destroy (which also abandons an unfinished recording). A graph is

@@ -141,15 +141,56 @@ def _i32_tensor(t: torch.Tensor, name: str) -> None:
     _require(t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be contiguous int32")
 
 
+def _on_device(*named) -> None:
+    """Every tensor the kernels dereference must live in device memory: a host pointer
+    handed to a kernel is a memory fault, not an error status."""
+    for name, t in named:
+        _require(t.is_cuda, f"{name} must be a device tensor")
+
+
+def _pools_match(k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride()
+             and v_cache.dtype == k_cache.dtype, "K/V pools differ in shape, stride or dtype")
+
+
+def _attn_args(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_tables: torch.Tensor, lens: torch.Tensor, hkv: int, d: int, fp8: bool,
+               lens_name: str = "context_lens", row_per_seq: bool = True) -> None:
+    """Checks shared by the attention calls, done before any launch: the C ABI takes the
+    element size from the query type and trusts every size below, so a mismatch here would
+    make the kernels address past the buffers."""
+    _pools_match(k_cache, v_cache)
+    _require(query.dim() == 3 and query.is_contiguous() and out.is_contiguous()
+             and query.shape == out.shape, "query/out must be contiguous [rows, H_q, D] of one shape")
+    _require(out.dtype == query.dtype, "out must have the query's dtype")
+    if fp8:
+        _require(query.dtype in (torch.float16, torch.bfloat16), "an FP8 cache is read with f16 or bf16 queries")
+    else:
+        _require(query.dtype == k_cache.dtype, "query dtype must equal the pool dtype")
+    _require(query.shape[2] == d, f"query head_dim {query.shape[2]} != pool head_dim {d}")
+    _require(query.shape[1] % hkv == 0, "num_q_heads must be a multiple of the pool's num_kv_heads")
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(lens, lens_name)
+    _require(block_tables.dim() == 2, "block_tables must be [num_seqs, stride]")
+    _require(lens.dim() == 1 and block_tables.shape[0] == lens.numel(),
+             f"block_tables has {block_tables.shape[0]} rows for {lens.numel()} {lens_name}")
+    if row_per_seq:                               # decode: one query row per sequence
+        _require(query.shape[0] == lens.numel(), "query rows must equal the number of sequences")
+    _on_device(("out", out), ("query", query), ("k_cache", k_cache), ("v_cache", v_cache),
+               ("block_tables", block_tables), (lens_name, lens))
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
                       v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
     """Write ``key``/``value`` ``[T, H_kv, D]`` rows into the pools at ``slot_mapping``."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
-    _require(key.shape == value.shape and key.stride() == value.stride(), "key/value differ")
-    _require(key.dim() == 3 and key.stride(2) == 1 and key.stride(1) == d, "key rows must be [H_kv, D] contiguous")
+    _pools_match(k_cache, v_cache)
+    _new_rows(key, value, hkv, d)
+    _require(key.dtype == k_cache.dtype, "key dtype must equal the pool dtype")
     _i32_tensor(slot_mapping, "slot_mapping")
     _require(slot_mapping.numel() == key.shape[0], "slot_mapping length")
+    _on_device(("key", key), ("value", value), ("k_cache", k_cache), ("v_cache", v_cache),
+               ("slot_mapping", slot_mapping))
     _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
         _ptr(key), _ptr(value), key.stride(0), _ptr(k_cache), _ptr(v_cache), bstride, nb,
         _ptr(slot_mapping), key.shape[0], hkv, d, bs, _dtype(k_cache), _stream(stream)))
@@ -159,9 +200,7 @@ def decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_cach
            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, stream=None) -> None:
     """Single-pass paged decode attention; ``out``/``query`` are ``[B, H_q, D]``."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=False)
     B, hq, _ = query.shape
     _check("pa_decode", lib().pa_decode(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
@@ -182,13 +221,9 @@ def decode_splitkv(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor
     """Split-KV decode with a log-sum-exp merge. ``workspace`` is a device byte
     tensor of at least ``splitkv_workspace_bytes(...)`` bytes (allocated here if None)."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=False)
     B, hq, _ = query.shape
-    need = splitkv_workspace_bytes(B, hq, d, max(max_context_len, 1), partition_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    workspace = _workspace(workspace, B, hq, d, max_context_len, partition_size, query.device)
     _check("pa_decode_splitkv", lib().pa_decode_splitkv(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
@@ -196,10 +231,29 @@ def decode_splitkv(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor
         _stream(stream)))
 
 
-def _step_rows(key_new: torch.Tensor, value_new: torch.Tensor, B: int, hkv: int, d: int):
-    _require(key_new.shape == value_new.shape and key_new.stride() == value_new.stride(), "key_new/value_new differ")
-    _require(key_new.dim() == 3 and key_new.shape[0] == B and key_new.shape[1] == hkv and key_new.shape[2] == d
-             and key_new.stride(2) == 1 and key_new.stride(1) == d, "new rows must be [B, H_kv, D], rows contiguous")
+def _new_rows(key: torch.Tensor, value: torch.Tensor, hkv: int, d: int) -> None:
+    """New-token rows ``[T, H_kv, D]`` (heads and dims contiguous, any row stride)."""
+    _require(key.shape == value.shape and key.stride() == value.stride() and key.dtype == value.dtype,
+             "key/value differ in shape, stride or dtype")
+    _require(key.dim() == 3 and key.shape[1] == hkv and key.shape[2] == d and key.stride(2) == 1
+             and key.stride(1) == d, f"new rows must be [T, {hkv}, {d}] with [H_kv, D] contiguous")
+
+
+def _step_rows(key_new: torch.Tensor, value_new: torch.Tensor, query: torch.Tensor, B: int, hkv: int, d: int):
+    _new_rows(key_new, value_new, hkv, d)
+    _require(key_new.shape[0] == B, "one new row per sequence")
+    _require(key_new.dtype == query.dtype, "new rows must have the query's dtype")
+    _on_device(("key_new", key_new), ("value_new", value_new))
+
+
+def _workspace(workspace: Optional[torch.Tensor], B: int, hq: int, d: int, max_context_len: int,
+               partition_size: int, device) -> torch.Tensor:
+    need = splitkv_workspace_bytes(B, hq, d, max(max_context_len, 1), partition_size)
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _on_device(("workspace", workspace))
+    _require(workspace.is_contiguous(), "workspace must be contiguous")
+    return workspace
 
 
 def decode_step(out: torch.Tensor, query: torch.Tensor, key_new: torch.Tensor, value_new: torch.Tensor,
@@ -208,12 +262,9 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_new: torch.Tensor, v
     """One decode step in one launch: row b of ``key_new``/``value_new`` goes to position
     ``context_lens[b] - 1`` through the table, then the single-pass decode."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _step_rows(key_new, value_new, query, query.shape[0], hkv, d)
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=False)
     B, hq, _ = query.shape
-    _step_rows(key_new, value_new, B, hkv, d)
     _check("pa_decode_step", lib().pa_decode_step(
         _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), key_new.stride(0), _ptr(k_cache), _ptr(v_cache),
         bstride, nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale,
@@ -226,11 +277,10 @@ def decode_step_fp8(out: torch.Tensor, query: torch.Tensor, key_new: torch.Tenso
                     stream=None) -> None:
     """``decode_step`` over FP8 pools: the new rows are quantised on the way in."""
     nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _step_rows(key_new, value_new, query, query.shape[0], hkv, d)
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=True)
     B, hq, _ = query.shape
-    _step_rows(key_new, value_new, B, hkv, d)
+    _on_device(("k_scale", k_scale), ("v_scale", v_scale))
     _check("pa_decode_step_fp8", lib().pa_decode_step_fp8(
         _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), key_new.stride(0), _ptr(k_cache), _ptr(v_cache),
         bstride, nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale,
@@ -284,7 +334,7 @@ def _fp8_pools(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tens
     """FP8 pools are uint8 tensors holding e4m3 codes; scales float32 ``[H_kv]``."""
     _require(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8, "FP8 pools must be uint8 (e4m3 codes)")
     dims = _pool_dims(k_cache)
-    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
+    _pools_match(k_cache, v_cache)
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
         _require(t.dtype == torch.float32 and t.is_contiguous() and t.numel() == dims[2],
                  f"{name} must be contiguous float32 [num_kv_heads]")
@@ -297,10 +347,11 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch
     """Quantise ``key``/``value`` ``[T, H_kv, D]`` rows to e4m3 with per-head scales and write
     them into the FP8 pools at ``slot_mapping``."""
     nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
-    _require(key.shape == value.shape and key.stride() == value.stride(), "key/value differ")
-    _require(key.dim() == 3 and key.stride(2) == 1 and key.stride(1) == d, "key rows must be [H_kv, D] contiguous")
+    _new_rows(key, value, hkv, d)
     _i32_tensor(slot_mapping, "slot_mapping")
     _require(slot_mapping.numel() == key.shape[0], "slot_mapping length")
+    _on_device(("key", key), ("value", value), ("slot_mapping", slot_mapping), ("k_cache", k_cache),
+               ("v_cache", v_cache), ("k_scale", k_scale), ("v_scale", v_scale))
     _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
         _ptr(key), _ptr(value), key.stride(0), _ptr(k_cache), _ptr(v_cache), bstride, nb,
         _ptr(slot_mapping), key.shape[0], hkv, d, bs, _ptr(k_scale), _ptr(v_scale), _dtype(key),
@@ -312,10 +363,9 @@ def decode_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor, v_
                v_scale: torch.Tensor, stream=None) -> None:
     """Single-pass paged decode over FP8 pools; ``out``/``query`` ``[B, H_q, D]`` in f16 or bf16."""
     nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=True)
     B, hq, _ = query.shape
+    _on_device(("k_scale", k_scale), ("v_scale", v_scale))
     _check("pa_decode_fp8", lib().pa_decode_fp8(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _ptr(k_scale), _ptr(v_scale),
@@ -329,13 +379,10 @@ def decode_splitkv_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
                        stream=None) -> None:
     """Split-KV decode over FP8 pools (workspace as ``decode_splitkv``)."""
     nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(context_lens, "context_lens")
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=True)
     B, hq, _ = query.shape
-    need = splitkv_workspace_bytes(B, hq, d, max(max_context_len, 1), partition_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    workspace = _workspace(workspace, B, hq, d, max_context_len, partition_size, query.device)
+    _on_device(("k_scale", k_scale), ("v_scale", v_scale))
     _check("pa_decode_splitkv_fp8", lib().pa_decode_splitkv_fp8(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _ptr(k_scale), _ptr(v_scale),
@@ -343,15 +390,21 @@ def decode_splitkv_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def _chunk_offsets(cu_q_lens: torch.Tensor, seq_lens: torch.Tensor) -> None:
+    _i32_tensor(cu_q_lens, "cu_q_lens")
+    _require(cu_q_lens.dim() == 1 and cu_q_lens.numel() == seq_lens.numel() + 1,
+             "cu_q_lens must hold num_seqs + 1 offsets")
+
+
 def prefill_chunked(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
                     k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
                     seq_lens: torch.Tensor, scale: float, causal: bool = True, stream=None) -> None:
     """Chunked (causal) prefill over the paged cache; ``out``/``query`` are ``[T, H_q, D]``."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(cu_q_lens, "cu_q_lens")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(seq_lens, "seq_lens")
+    _chunk_offsets(cu_q_lens, seq_lens)
+    _attn_args(out, query, k_cache, v_cache, block_tables, seq_lens, hkv, d, fp8=False, lens_name="seq_lens",
+               row_per_seq=False)
+    _on_device(("cu_q_lens", cu_q_lens))
     T, hq, _ = query.shape
     _check("pa_prefill_chunked", lib().pa_prefill_chunked(
         _ptr(out), _ptr(query), _ptr(cu_q_lens), max_q_len, T, _ptr(k_cache), _ptr(v_cache), bstride,
@@ -365,11 +418,12 @@ def prefill_chunked_fp8(out: torch.Tensor, query: torch.Tensor, cu_q_lens: torch
                         causal: bool = True, stream=None) -> None:
     """Chunked (causal) prefill over FP8 pools; ``out``/``query`` ``[T, H_q, D]`` in f16 or bf16."""
     nb, bs, hkv, d, bstride = _fp8_pools(k_cache, v_cache, k_scale, v_scale)
-    _require(query.is_contiguous() and out.is_contiguous() and query.shape == out.shape, "query/out")
-    _i32_tensor(cu_q_lens, "cu_q_lens")
-    _i32_tensor(block_tables, "block_tables")
-    _i32_tensor(seq_lens, "seq_lens")
+    _chunk_offsets(cu_q_lens, seq_lens)
+    _attn_args(out, query, k_cache, v_cache, block_tables, seq_lens, hkv, d, fp8=True, lens_name="seq_lens",
+               row_per_seq=False)
+    _on_device(("cu_q_lens", cu_q_lens))
     T, hq, _ = query.shape
+    _on_device(("k_scale", k_scale), ("v_scale", v_scale))
     _check("pa_prefill_chunked_fp8", lib().pa_prefill_chunked_fp8(
         _ptr(out), _ptr(query), _ptr(cu_q_lens), max_q_len, T, _ptr(k_cache), _ptr(v_cache), bstride,
         nb, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), seq_lens.numel(), hq, hkv, d,
@@ -380,9 +434,10 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tenso
     """Copy-on-write on the device: block ``dst`` of both pools becomes block ``src`` for each
     ``(src, dst)`` row of ``pairs`` (int32 ``[n, 2]`` on the device)."""
     nb, bs, hkv, d, bstride = _pool_dims(k_cache)
-    _require(v_cache.shape == k_cache.shape and v_cache.stride() == k_cache.stride(), "K/V pools differ")
+    _pools_match(k_cache, v_cache)
     _i32_tensor(pairs, "pairs")
     _require(pairs.dim() == 2 and pairs.shape[1] == 2 and pairs.is_cuda, "pairs must be [n, 2] on the device")
+    _on_device(("k_cache", k_cache), ("v_cache", v_cache))
     _check("pa_copy_blocks", lib().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), bstride, nb, hkv, d, _dtype(k_cache),
         _ptr(pairs) if pairs.numel() else None, pairs.shape[0], _stream(stream)))

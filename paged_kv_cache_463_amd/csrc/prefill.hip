@@ -227,6 +227,23 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     bid = (blk < nblk_valid && bid >= 0 && bid < p.num_blocks) ? bid : 0;
     return (int64_t)bid * p.block_stride_bytes;
   };
+  // Blocks of tile t (bit k: logical block 4t+k) that hold visible keys but have
+  // no valid table entry (an id outside the pool, or past the table's stride):
+  // they are read as block 0, so their scores are masked and their V rows
+  // zeroed, as for keys past the end. A precondition violation; this only
+  // keeps other sequences' rows out of the result.
+  auto tile_bad = [&](int t) -> int {
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < kBK / kBlockSize; ++k) {
+      const int blk = t * (kBK / kBlockSize) + k;
+      if (blk * kBlockSize < kend) {
+        const int bid = blk < p.block_table_stride ? tbl[blk] : -1;
+        if (bid < 0 || bid >= p.num_blocks) bad |= 1 << k;
+      }
+    }
+    return bad;
+  };
   // One direct global -> LDS load of 16 bytes per lane: M0 holds the LDS
   // destination of lane 0 (lane i writes 16 bytes further per lane), the
   // global address is a scalar block base plus a 32-bit lane offset. Issued as
@@ -248,6 +265,11 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     return {kc + block_base(tk, kbid), vc + block_base(tv, vbid), &sK[kb][wave * kBlockSize * RB],
             &sV[vb][wave * kBlockSize * RB]};
   };
+  // this wave's block of V tile tv is a valid pool block (else its rows are zeroed on landing)
+  auto v_ok = [&](int tv, int vbid) -> bool {
+    const int blk = min(tv, nkt - 1) * (kBK / kBlockSize) + wave;
+    return blk >= p.block_table_stride || blk * kBlockSize >= kend || (vbid >= 0 && vbid < p.num_blocks);
+  };
   auto dma_part = [&](const DmaJob& j, int n) {      // n in [0, NPARTS)
     if constexpr (F8) {
       if (n == 0) {
@@ -267,8 +289,9 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     for (int n = 0; n < NPARTS; ++n) dma_part(j, n);
   };
   // wait for this wave's loads; in the last V tile zero the rows of keys past
-  // kend (stale slots) in this wave's block, then make everything visible
-  auto land = [&](int tv, int vb) {
+  // kend (stale slots) in this wave's block, and all rows of a block without a
+  // valid table entry, then make everything visible
+  auto land = [&](int tv, int vb, bool vok) {
     if constexpr (F8) {                      // widen this wave's rows into the 16-bit layout
 #pragma unroll
       for (int i = 0; i < NL8; ++i) {
@@ -283,11 +306,12 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (tv < nkt && tv * kBK + kBK > kend) {
+    const bool blk_ok = vok && tv * (kBK / kBlockSize) + wave < p.block_table_stride;
+    if (tv < nkt && (tv * kBK + kBK > kend || !blk_ok)) {
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
         const int r = (n * 1024 + 16 * lane) / RB;
-        if (tv * kBK + wave * kBlockSize + r >= kend)
+        if (tv * kBK + wave * kBlockSize + r >= kend || !blk_ok)
           *reinterpret_cast<u32x4*>(&sV[vb][wave * kBlockSize * RB + n * 1024 + 16 * lane]) = u32x4{0u, 0u, 0u, 0u};
       }
     }
@@ -311,10 +335,11 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
   // and V(t+1) into the other two buffers; one barrier per tile.
   f32x16 sa[2], sb[2];                       // scores of two consecutive tiles
   dma(0, entry(0), 0, 0, entry(0), 0);
-  land(0, 0);
+  land(0, 0, v_ok(0, entry(0)));
   dma(1, entry(1), 1, nkt, entry(nkt), 1);    // K(1); the V part re-reads tile nkt-1 into sV[1]
   // table entries for the loads of the next iteration, read a tile ahead
   int kbid_next = entry(2), vbid_next = entry(1);
+  int bad_cur = tile_bad(0);                 // blocks of the scored tile without a valid entry
   {
     const uint8_t* K0 = sK[0];
 #pragma unroll
@@ -328,7 +353,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
                         qreg[ds], sa[kt]);
     }
   }
-  land(nkt, 1);
+  land(nkt, 1, true);
 
   // one tile; sc holds the scores of tile t, sn receives those of tile t+1.
   // The loop below runs two tiles per trip with the two score arrays trading
@@ -336,17 +361,19 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
   auto key_tile = [&](const int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int key0 = t * kBK;
     const DmaJob job = dma_job(t + 2, kbid_next, t & 1, t + 1, vbid_next, (t + 1) & 1);
+    const bool vok_next = v_ok(t + 1, vbid_next);
 
     // scale; mask (uniform: only tiles that reach the causal diagonal or the
-    // end of the keys); tile max of the column; rare rescale
-    const bool edge = (key0 + kBK > kend) || (p.causal && key0 + kBK - 1 > s0 + q0);
+    // end of the keys, or hold a block without a valid table entry); tile max
+    // of the column; rare rescale
+    const bool edge = (key0 + kBK > kend) || (p.causal && key0 + kBK - 1 > s0 + q0) || bad_cur != 0;
     if (edge) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool vis = key < kend && (!p.causal || key <= pabs);
+          const bool vis = key < kend && (!p.causal || key <= pabs) && !((bad_cur >> (2 * kt + (r >> 3))) & 1);
           sc[kt][r] = vis ? sc[kt][r] : -INFINITY;
         }
     }
@@ -473,7 +500,8 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     }
     kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
     vbid_next = entry(t + 2);                 // loads complete during the wait below
-    land(t + 1, (t + 1) & 1);
+    bad_cur = t + 1 < nkt ? tile_bad(t + 1) : 0;
+    land(t + 1, (t + 1) & 1, vok_next);
   };
   int t = 0;
   for (; t + 1 < nkt; t += 2) {

@@ -219,18 +219,17 @@ def test_fp8_llama3_8b_gqa_full_size():
     assert_close(out_f64(out), x.oracle(rk, rv), "bf16", "fp8 llama3-8b full size")
 
 
-def test_fp8_long_context_splitkv_full_size_sampled():
+def test_fp8_long_context_splitkv_full_size():
+    """The long-context shapes over an FP8 cache, every sequence and head against the oracle."""
     case = W.long_context_bf16()
-    order = np.argsort(case.context_lens)
-    seqs = sorted({int(order[0]), int(order[-1]), 3})
-    say(f"case: fp8 cache, long-context split-KV, sampled sequences {seqs}")
+    say("case: fp8 cache, long-context split-KV, all sequences")
     x = DeviceFp8(case, seed=9)
     x.scatter()
     out = x.decode(split=512)
     torch.cuda.synchronize()
     rk, rv = x.check_scatter()
     x.kp = x.vp = None                                       # free the device pools first
-    assert_close(out_f64(out)[seqs], x.oracle(rk, rv, seqs), "bf16", "fp8 long-context split-KV")
+    assert_close(out_f64(out), x.oracle(rk, rv), "bf16", "fp8 long-context split-KV, all sequences")
 
 
 # ---------------------------------------------------------------------------
@@ -307,17 +306,12 @@ def test_prefill_fp8_equals_16bit_prefill_of_the_same_values():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_prefill_fp8_chunked_prefill_shapes_sampled():
+def test_prefill_fp8_chunked_prefill_shapes_full_size():
     """The chunked-prefill workload's shapes (16 sequences, 2048 cached + 512 new tokens, 32/8
-    heads, head_dim 128) over an FP8 cache; sampled sequences and heads against the oracle."""
+    heads, head_dim 128) over an FP8 cache; every query row and head against the oracle."""
     case = W.chunked_prefill_bf16()
-    say("case: fp8 prefill at the chunked-prefill workload's shapes, sampled")
+    say("case: fp8 prefill at the chunked-prefill workload's shapes, full size")
     x = DeviceFp8Prefill(case, seed=13)
     out = x.run(True)
     torch.cuda.synchronize()
-    seqs, heads = [0, 9, 15], [0, 5, 31]
-    ref = x.oracle(True, seqs=seqs, heads=heads)
-    rows = np.concatenate([np.arange(case.cu_q_lens[b], case.cu_q_lens[b + 1]) for b in seqs])
-    got = out_f64(out)
-    assert not np.isnan(got).any()
-    assert_close(got[rows][:, heads], ref[rows][:, heads], "bf16", "fp8 prefill, sampled")
+    assert_close(out_f64(out), x.oracle(True), "bf16", "fp8 prefill, full size")

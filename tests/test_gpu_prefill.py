@@ -72,9 +72,9 @@ def test_prefill_long_chunk_many_tiles():
     _check(W.make_prefill("long", "bf16", [700, 0, 1031], [513, 1100, 257], 32, 8, 128, seed=320))
 
 
-def test_chunked_prefill_full_size_sampled():
-    case = W.chunked_prefill_bf16()
-    _check(case, seqs=[0, 7, 15], heads=list(range(case.num_q_heads)))
+def test_chunked_prefill_full_size():
+    """16 sequences x (2048 cached + 512 new tokens), 32/8 heads: every query row and head."""
+    _check(W.chunked_prefill_bf16())
 
 
 def test_prefill_causality_bitwise():
@@ -142,3 +142,38 @@ def test_chunk_offsets_past_the_query_rows_stay_in_bounds():
                                case.scale, case.num_kv_heads, case.dtype, causal=True, seqs=[0, 1])
     assert_close(out_f64(obig[:164]), ref[:164], "bf16", "chunks inside the rows")
     assert not bool(torch.isnan(obig[164:rows]).any())
+
+
+def test_invalid_table_entry_inside_the_visible_keys_is_masked():
+    """A table entry outside the pool inside the visible range (a precondition violation) is
+    read as block 0 and masked: its 16 keys take no part in the softmax. Sequence 0's logical
+    block 1 (keys 16..31) gets id -1 and sequence 1's logical block 2 an id past the pool; every
+    query row must equal the attention over its visible keys without those 16 (computed from
+    the oracle's gather and attend), and nothing else may change."""
+    case = W.make_prefill("badentry", "bf16", [40, 50], [30, 20], 8, 2, 128, seed=92)
+    d = DevicePrefill(case)
+    P.reshape_and_cache(d.kn, d.vn, d.kp, d.vp, d.slots)
+    bad = {0: 1, 1: 2}                                   # sequence -> logical block with a bad id
+    bt = case.block_tables.copy()
+    bt[0, 1] = -1
+    bt[1, 2] = case.num_blocks + 7
+    say("case: prefill with out-of-range table entries inside the visible keys")
+    P.prefill_chunked(d.out, d.q, d.cu, case.max_q_len, d.kp, d.vp, i32(bt), d.lens, case.scale, True)
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    got = out_f64(d.out)
+    ref = np.zeros_like(got)
+    sc = float(np.float32(case.scale))
+    G = case.num_q_heads // case.num_kv_heads
+    for b, blk in bad.items():
+        L, q0, q1 = int(case.seq_lens[b]), int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
+        K = oracle.to_f64(oracle.gather(kp, case.block_tables[b], L), "bf16")
+        V = oracle.to_f64(oracle.gather(vp, case.block_tables[b], L), "bf16")
+        vis = oracle.visible_keys(L, q1 - q0, True)
+        vis[:, 16 * blk:16 * blk + 16] = False
+        Q = oracle.to_f64(case.query[q0:q1], "bf16")
+        for i in range(q1 - q0):
+            for h in range(case.num_q_heads):
+                g = h // G
+                ref[q0 + i, h] = oracle.attend(Q[i, h], K[vis[i], g], V[vis[i], g], sc)
+    assert_close(got, ref, "bf16", "prefill with masked bad table entries")

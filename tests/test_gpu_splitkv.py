@@ -99,8 +99,8 @@ def test_splitkv_item_modes_agree_with_oracle(dtype, G, D):
 def test_llama3_gqa_full_size_workgroup_items():
     """The GQA batch at full size (256 sequences, a shared 512-token prefix for half of them) in
     512-token partitions (8 partitions planned): the persistent workgroups take many items each.
-    Sequences up to 512 tokens are written directly and equal the single pass bit for bit; a
-    sample of the longer ones, including the longest, is checked against the oracle."""
+    Sequences up to 512 tokens are written directly and equal the single pass bit for bit; every
+    sequence and head is compared with the oracle."""
     case = W.llama3_8b_gqa_bf16()
     say(f"case: llama3 GQA split-KV workgroup items, max len {case.max_context_len}")
     d = DeviceDecode(case)
@@ -112,12 +112,9 @@ def test_llama3_gqa_full_size_workgroup_items():
     short = torch.from_numpy(np.nonzero((lens > 0) & (lens <= 512))[0]).cuda()
     assert short.numel() > 0
     assert torch.equal(grp[short].view(torch.int16), one[short].view(torch.int16))
-    assert not torch.isnan(grp).any()
-    order = np.argsort(lens)
-    seqs = sorted({int(order[-1]), int(order[-2]), int(order[len(order) // 2 + 10]), int(order[-40])})
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     del d
-    assert_close(out_f64(grp)[seqs], oracle_decode(case, kp, vp, seqs), "bf16", "GQA split-KV, sampled")
+    assert_close(out_f64(grp), oracle_decode(case, kp, vp), "bf16", "GQA split-KV, all sequences")
 
 
 def test_splitkv_rerun_and_block_relabelling_bit_identical():
@@ -164,18 +161,18 @@ def test_workspace_too_small_is_rejected():
     assert e.value.status == 5
 
 
-def test_long_context_bf16_full_size_sampled():
+def test_long_context_bf16_full_size():
+    """The long-context batch at full size (8 sequences of 32k-131k tokens, 64 query / 8 kv heads,
+    512-token partitions, wave items): every sequence and head against the oracle."""
     case = W.long_context_bf16()
-    order = np.argsort(case.context_lens)
-    seqs = sorted({int(order[0]), int(order[-1]), 3})
-    say(f"case: long context split-KV, sampled sequences {seqs}, lens {case.context_lens.tolist()}")
+    say(f"case: long context split-KV, all sequences, lens {case.context_lens.tolist()}")
     d = DeviceDecode(case)
     d.scatter()
     out = d.decode(split=512)
     torch.cuda.synchronize()
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     del d
-    assert_close(out_f64(out)[seqs], oracle_decode(case, kp, vp, seqs), "bf16", "long-context split-KV")
+    assert_close(out_f64(out), oracle_decode(case, kp, vp), "bf16", "long-context split-KV, all sequences")
 
 
 @pytest.mark.parametrize("part", [512, 32])        # 2 partitions planned: workgroup items; 32: wave items
