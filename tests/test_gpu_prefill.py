@@ -169,7 +169,7 @@ def test_invalid_table_entry_inside_the_visible_keys_is_masked():
         L, q0, q1 = int(case.seq_lens[b]), int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
         K = oracle.to_f64(oracle.gather(kp, case.block_tables[b], L), "bf16")
         V = oracle.to_f64(oracle.gather(vp, case.block_tables[b], L), "bf16")
-        vis = oracle.visible_keys(L, q1 - q0, True)
+        vis = oracle.paged_attention.visible_keys(L, q1 - q0, True)
         vis[:, 16 * blk:16 * blk + 16] = False
         Q = oracle.to_f64(case.query[q0:q1], "bf16")
         for i in range(q1 - q0):

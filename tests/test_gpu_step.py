@@ -157,14 +157,14 @@ def test_splitkv_graph_replays_while_lengths_grow(plan):
     bound = case.max_context_len if plan == "group" else 20 * 512
     ws = torch.empty(P.splitkv_workspace_bytes(case.num_seqs, 16, 128, bound, 512), dtype=torch.uint8,
                      device="cuda")
-    lens_dev = i32(np.asarray(final) - 600)              # the lengths at capture
+    lens_dev = i32(np.maximum(np.asarray(final) - 600, 1))   # the lengths at capture
     out = torch.full_like(d.out, float("nan"))
     say(f"case: split-KV graph ({plan} items) replayed while lengths grow to {final}")
     with P.StepGraph() as graph:
         P.decode_splitkv(out, d.q, d.kp, d.vp, d.bt, lens_dev, case.scale, bound, 512, ws, stream=graph.stream)
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     for grow in (600, 300, 1, 0):
-        lens = (np.asarray(final) - grow).astype(np.int32)
+        lens = np.maximum(np.asarray(final) - grow, 1).astype(np.int32)
         lens_dev.copy_(torch.from_numpy(lens))
         torch.cuda.synchronize()
         graph.replay()
