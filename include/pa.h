@@ -78,7 +78,8 @@ typedef enum {
   PA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch         */
   PA_ERR_ALIGNMENT = 7,    /* a pointer or stride is not 16-byte aligned          */
   PA_ERR_NO_BLOCKS = 8,    /* block manager: not enough free blocks (no change)   */
-  PA_ERR_SEQUENCE = 9      /* block manager: unknown request id, or one in use    */
+  PA_ERR_SEQUENCE = 9,     /* block manager: unknown request id, or one in use    */
+  PA_ERR_SCRATCH = 10      /* needs more than the static split-KV scratch holds   */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
@@ -178,6 +179,35 @@ PA_API int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cac
                           int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
                           int32_t max_context_len, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_splitkv_noalloc — pa_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and results
+ * (bit for bit), with the workspace taken from a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES (80 MiB) that the library holds on every GPU it
+ * runs on until the process ends. The call allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine. Its first call on a device looks
+ * up that device's copy of the array.
+ *
+ * Arguments as pa_decode_splitkv without workspace / workspace_bytes. A call
+ * whose pa_decode_splitkv_workspace_bytes(...) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH and launches nothing (80 MiB
+ * covers, e.g., 8 sequences x 64 query heads of 131072-token contexts in
+ * 512-token partitions at head_dim 128, which need 65 MiB). The array keeps
+ * the last call's contents; every call resets what must start at zero (its
+ * work counter) with a kernel of its own. All calls on one GPU share the one
+ * array: calls that overlap in time on that GPU (different streams, or host
+ * threads without ordering) race and give undefined results.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+PA_API int32_t pa_decode_splitkv_noalloc(void* out, const void* query, const void* k_cache,
+                                         const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                                         const int32_t* block_tables, int32_t block_table_stride,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, float scale, int32_t dtype,
+                                         int32_t max_context_len, int32_t partition_size, void* stream);
 
 /*
  * pa_decode_step — one whole decode step in one launch: each sequence's new

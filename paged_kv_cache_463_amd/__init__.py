@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     decode_step_fp8,
     decode_splitkv,
     decode_splitkv_fp8,
+    decode_splitkv_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     lib,
     prefill_chunked,
     prefill_chunked_fp8,
@@ -29,6 +31,6 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
            "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8", "decode_step", "decode_step_fp8",
-           "StepGraph",
+           "decode_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "StepGraph",
            "prefill_chunked", "prefill_chunked_fp8", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
            "LibraryNotBuilt", "PagedAttentionError"]

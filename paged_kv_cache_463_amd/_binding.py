@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_PTR", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
                 4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP",
-                7: "PA_ERR_ALIGNMENT", 8: "PA_ERR_NO_BLOCKS", 9: "PA_ERR_SEQUENCE"}
+                7: "PA_ERR_ALIGNMENT", 8: "PA_ERR_NO_BLOCKS", 9: "PA_ERR_SEQUENCE", 10: "PA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 80 << 20              # PA_NOALLOC_SCRATCH_BYTES of include/pa.h
 PA_ERR_NO_BLOCKS, PA_ERR_SEQUENCE = 8, 9
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
@@ -35,6 +36,8 @@ SIGNATURES = {
     "pa_decode_splitkv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_splitkv": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
+    "pa_decode_splitkv_noalloc": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _i32, _i32, _i32, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
     "pa_prefill_chunked_fp8": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
@@ -229,6 +232,21 @@ def decode_splitkv(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
         max_context_len, partition_size, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def decode_splitkv_noalloc(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, max_context_len: int, partition_size: int = 512,
+                           stream=None) -> None:
+    """``decode_splitkv`` with the library's static device scratch as its workspace: nothing is
+    allocated, here or in the library. Calls that overlap on one GPU race on that scratch."""
+    nb, bs, hkv, d, bstride = _pool_dims(k_cache)
+    _attn_args(out, query, k_cache, v_cache, block_tables, context_lens, hkv, d, fp8=False)
+    B, hq, _ = query.shape
+    _check("pa_decode_splitkv_noalloc", lib().pa_decode_splitkv_noalloc(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
+        max_context_len, partition_size, _stream(stream)))
 
 
 def _new_rows(key: torch.Tensor, value: torch.Tensor, hkv: int, d: int) -> None:

@@ -10,9 +10,11 @@
 
 #include "pa_launch.h"
 
+static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kScratchBytes, "header and library agree on the scratch size");
+
 namespace {
 
-constexpr int32_t kVersion = 300;  // 0.3.0
+constexpr int32_t kVersion = 301;  // 0.3.1
 
 int elem_bytes(int32_t dtype) {
   switch (dtype) {
@@ -136,6 +138,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent size or stride";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: block_size, head_dim or group not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-KV workspace missing or too small";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more split-KV scratch than the library's static array holds";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch error";
     case PA_ERR_ALIGNMENT: return "PA_ERR_ALIGNMENT: pointer or stride not 16-byte aligned";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks";
@@ -299,6 +303,32 @@ int32_t pa_decode_splitkv(void* out, const void* query, const void* k_cache, con
                                           num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
                                           dtype);
   carve_splitkv(p, workspace, mcl, partition_size);
+  return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_splitkv_noalloc(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                  int64_t block_stride, int64_t num_blocks, const int32_t* block_tables,
+                                  int32_t block_table_stride, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                                  int32_t max_context_len, int32_t partition_size, void* stream) {
+  int32_t st = check_attention_common(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                      block_tables, block_table_stride, context_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  const int32_t mcl = max_context_len > 0 ? max_context_len : 1;
+  if (pa_decode_splitkv_workspace_bytes(num_seqs, num_q_heads, head_dim, mcl, partition_size) >
+      pa::kScratchBytes)
+    return PA_ERR_SCRATCH;
+  void* scratch = nullptr;                  // this device's copy of the static array
+  if (pa::scratch_device_ptr(&scratch) != hipSuccess) return PA_ERR_HIP;
+  pa::DecodeParams p = make_decode_params(out, query, k_cache, v_cache, block_stride, num_blocks,
+                                          block_tables, block_table_stride, context_lens,
+                                          num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                                          dtype);
+  carve_splitkv(p, scratch, mcl, partition_size);
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 

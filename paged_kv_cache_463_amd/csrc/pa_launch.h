@@ -108,6 +108,11 @@ hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s);
 hipError_t launch_swap_chunk(const SwapChunk& c, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s);
+
+// Static split-KV scratch of pa_decode_splitkv_noalloc (splitkv_scratch.hip):
+// its size, and its address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(80) << 20;
+hipError_t scratch_device_ptr(void** out);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // chunked prefill over an FP8 (e4m3) cache: per-kv-head dequantisation scales
 hipError_t launch_prefill_fp8(const PrefillParams& p, const float* k_scale, const float* v_scale, hipStream_t s);

@@ -1,0 +1,66 @@
+"""pa_decode_splitkv_noalloc: the split-KV decode with the library's static device scratch as its
+workspace, for callers that cannot allocate. It must give the same bits as pa_decode_splitkv on
+the same inputs (same kernels, same plan), across consecutive calls that reuse the scratch —
+the second with a smaller batch, so stale partials and a stale work counter from the first call
+would show — and stay within tolerance of the oracle. Sizes beyond the scratch are refused
+before anything is launched."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_463_amd as P
+import workloads as W
+from gpu_cases import DeviceDecode, assert_close, assert_scatter_exact, oracle_decode, out_f64, say
+
+
+def test_noalloc_refuses_sizes_beyond_the_scratch():
+    """Host-side check only (fake, aligned, never-dereferenced pointers): 80 MiB is exceeded by
+    64 sequences x 64 query heads x 131072 tokens in 512-token partitions, so the call returns
+    PA_ERR_SCRATCH before touching the GPU; a zero-sequence call returns PA_OK."""
+    lib = P.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    need = P.splitkv_workspace_bytes(64, 64, 128, 131072, 512)
+    assert need > P.NOALLOC_SCRATCH_BYTES
+    st = lib.pa_decode_splitkv_noalloc(fake, fake, fake, fake, 16 * 8 * 128, 1000, fake, 8192, fake, 64, 64, 8,
+                                       128, 16, 0.088, 2, 131072, 512, None)
+    assert st == 10 and lib.pa_status_string(st).decode().startswith("PA_ERR_SCRATCH")
+    assert lib.pa_decode_splitkv_noalloc(fake, fake, fake, fake, 16 * 8 * 128, 1000, fake, 8192, fake, 0, 64, 8,
+                                         128, 16, 0.088, 2, 131072, 512, None) == 0
+    assert lib.pa_decode_splitkv_noalloc(fake, fake, fake, fake, 16 * 8 * 128, 1000, fake, 8192, fake, 4, 64, 8,
+                                         128, 16, 0.088, 2, 4096, 500, None) == 3    # partition not a multiple of 16
+
+
+def _pair(case, part, mcl):
+    say(f"case: noalloc vs workspace split-KV, B={case.num_seqs} G={case.group} part={part} mcl={mcl}")
+    d = DeviceDecode(case)
+    d.scatter()
+    ref = d.decode(split=part, out=torch.full_like(d.q, float("nan")), mcl=mcl).clone()
+    got = torch.full_like(d.q, float("nan"))
+    P.decode_splitkv_noalloc(got, d.q, d.kp, d.vp, d.bt, d.lens, case.scale, mcl, part)
+    torch.cuda.synchronize()
+    kp, vp = assert_scatter_exact(case, d.kp, d.vp)
+    bits = torch.int32 if case.dtype == "f32" else torch.int16
+    assert torch.equal(got.view(bits), ref.view(bits)), "noalloc differs from the workspace call"
+    assert_close(out_f64(got), oracle_decode(case, kp, vp), case.dtype, "noalloc vs oracle")
+
+
+@pytest.mark.gpu
+def test_noalloc_equals_workspace_call_on_consecutive_calls():
+    """First a long-context batch planned as wave items (many partitions per sequence), then a
+    smaller batch planned as workgroup items; both through the same static scratch."""
+    big = W.make_decode("noalloc1", "bf16", [20000, 513, 9000, 16, 31000, 1], 32, 4, 128, seed=71)
+    _pair(big, 512, big.max_context_len)
+    small = W.make_decode("noalloc2", "bf16", [700, 3, 1500], 16, 2, 128, seed=72)
+    _pair(small, 512, small.max_context_len)
+
+
+@pytest.mark.gpu
+def test_noalloc_long_context_shapes():
+    """The long-context workload's shapes (8 sequences of 32k-131k tokens, 64/8 heads,
+    512-token partitions: 63 MiB of scratch), then a small fp16 batch."""
+    case = W.long_context_bf16()
+    _pair(case, 512, case.max_context_len)
+    small = W.make_decode("noalloc3", "f16", [100, 2000], 8, 8, 128, seed=73)
+    _pair(small, 64, small.max_context_len)
