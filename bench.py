@@ -8,11 +8,18 @@ walks its layers, so repeated steps are not served from the 256 MB
 last-level cache. Inputs are seeded synthetic tensors resident in HBM before
 the timed region starts.
 
-Prints ONE JSON line: value = sequence-steps per second (decode) or query
-tokens per second (prefill) for the whole job, plus the roofline of the
-dominant kernel (algorithmic bytes or flops per launch divided by its average
-duration, measured with HIP events on the launch stream inside the timed
-region) and the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line. By default its headline is the long-context split-KV
+decode (8 sequences of 32k-131k tokens, the largest decode workload on one
+GPU), and the tiny fp32 decode, the Llama-2-7B-like fp16 decode, the
+Llama-3-8B-like GQA decode and the chunked prefill ride along as records of
+the same line (``configs``); ``--workload`` times one workload alone. Per
+workload: value = sequence-steps per second (decode) or query tokens per
+second (prefill) for the whole job, the roofline of the attention kernel
+(algorithmic bytes or flops per launch divided by its average duration,
+measured with HIP events on the launch stream inside the timed region), and
+the CPU oracle timed on a bounded sample of the same workload (worker
+processes over (sequence, kv head) units, one BLAS thread each, forked before
+this process touches the GPU).
 """
 from __future__ import annotations
 
@@ -59,7 +66,6 @@ WORKLOADS = {
     "long_ctx_fp8kv_splitkv_b8": ("long_context_bf16", "splitkv_fp8"),
     "chunked_prefill_fp8kv_16x2048p512": ("chunked_prefill_bf16", "prefill_fp8"),
 }
-DEFAULT_WORKLOAD = "llama2_7b_fp16_decode_b64"
 # block movement: name -> (pool blocks, kv heads, head_dim, copy pairs, swap blocks)
 BLOCK_WORKLOADS = {
     "cow_copy_bf16_2048x32k": (8192, 8, 128, 2048, 512),
@@ -145,7 +151,8 @@ def stored_traffic(workload: str, call: str, partition: int):
 # device state and one step
 # ----------------------------------------------------------------------------
 class Runner:
-    def __init__(self, case, call: str, layers: int, partition: int, step_mode: str = "separate"):
+    def __init__(self, case, call: str, layers: int, partition: int, step_mode: str = "separate",
+                 fp8_host=None):
         import torch
         import paged_kv_cache_463_amd as P
         import workloads as W
@@ -163,7 +170,7 @@ class Runner:
 
         self.fp8 = call.endswith("_fp8")
         if self.fp8:                                # e4m3 codes and per-head scales
-            f = W.fp8_pools(case, 0)
+            f = fp8_host if fp8_host is not None else W.fp8_pools(case, 0)
             k0, v0 = torch.from_numpy(f.k_pool).cuda(), torch.from_numpy(f.v_pool).cuda()
             self.ks, self.vs = torch.from_numpy(f.k_scale).cuda(), torch.from_numpy(f.v_scale).cuda()
             self.fp8_host = f
@@ -314,65 +321,121 @@ def time_steps(r: Runner, steps: int, warmup: int):
 
 
 # ----------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, on a bounded sample
+# CPU baseline: the oracle as it stands, over (sequence, kv head) units
 # ----------------------------------------------------------------------------
-def cpu_baseline(case, call: str, r: Runner, budget_s: float):
+# One unit = the oracle's decode (or prefill chunk) of one sequence restricted to one kv head's
+# G query heads, on the head's slice of the scattered pools. The units run in worker processes
+# forked before this process touches the GPU (so they share the host arrays and never open the
+# device), one BLAS thread each; the sample is every unit of whole passes over the batch, in a
+# seeded order, until a time budget is spent.
+_UNITS = None            # the host context of the workload being timed, read by the workers
+
+
+def _unit_ctx(case, call: str, fp8_host=None):
+    """Scattered host pools (the oracle's own scatter) and what the units need."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    if r.fp8:
-        f = r.fp8_host
-        kp, vp = oracle.fp8.scatter_fp8(f.k_pool, f.v_pool, case.k_new, case.v_new, case.slot_mapping,
-                                        f.k_scale, f.v_scale, case.dtype)
+    if fp8_host is not None:
+        kp, vp = oracle.fp8.scatter_fp8(fp8_host.k_pool, fp8_host.v_pool, case.k_new, case.v_new,
+                                        case.slot_mapping, fp8_host.k_scale, fp8_host.v_scale, case.dtype)
     else:
         kp, vp = oracle.scatter(case.k_pool, case.v_pool, case.k_new, case.v_new, case.slot_mapping)
-    gpu_out = r.out.float().cpu().double().numpy()
-    order = np.random.default_rng(0).permutation(case.num_seqs)
-    t0 = time.perf_counter()
-    done, units, err, passes = [], 0, 0.0, 0
-    while True:                                 # whole passes over the batch until the budget is spent
-        for b in order:
-            b = int(b)
-            if call.startswith("prefill"):
-                heads = list(range(case.num_q_heads))
-                if r.fp8:
-                    ref = oracle.fp8.paged_prefill_fp8(case.query, kp, vp, case.block_tables, case.seq_lens,
-                                                       case.cu_q_lens, case.scale, f.k_scale, f.v_scale,
-                                                       case.num_kv_heads, case.dtype, seqs=[b], heads=heads)
-                else:
-                    ref = oracle.paged_prefill(case.query, kp, vp, case.block_tables, case.seq_lens,
-                                               case.cu_q_lens, case.scale, case.num_kv_heads, case.dtype,
-                                               seqs=[b], heads=heads)
-                q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
-                err = max(err, float(np.abs(ref[q0:q1] - gpu_out[q0:q1]).max()))
-                units += q1 - q0
-            elif r.fp8:
-                ref = oracle.fp8.paged_decode_fp8(case.query[[b]], kp, vp, case.block_tables[[b]],
-                                                  case.context_lens[[b]], case.scale, f.k_scale, f.v_scale,
-                                                  case.num_kv_heads, case.dtype)
-                err = max(err, float(np.abs(ref[0] - gpu_out[b]).max()))
-                units += 1
-            else:
-                ref = oracle.paged_decode(case.query[[b]], kp, vp, case.block_tables[[b]], case.context_lens[[b]],
-                                          case.scale, case.num_kv_heads, case.dtype)
-                err = max(err, float(np.abs(ref[0] - gpu_out[b]).max()))
-                units += 1
-            done.append(b)
-            if time.perf_counter() - t0 > budget_s:
-                break
+    return {"case": case, "prefill": call.startswith("prefill"), "fp8": fp8_host, "kp": kp, "vp": vp}
+
+
+def _oracle_unit(bg):
+    """The oracle on unit (b, g); returns (b, g, float64 output rows [rows, G, D])."""
+    import oracle
+    b, g = bg
+    c = _UNITS
+    case, f = c["case"], c["fp8"]
+    G = case.num_q_heads // case.num_kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    kp, vp = c["kp"][:, :, g:g + 1], c["vp"][:, :, g:g + 1]
+    if c["prefill"]:
+        q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
+        args = (case.query[q0:q1, hs], kp, vp, case.block_tables[b:b + 1], case.seq_lens[b:b + 1],
+                np.array([0, q1 - q0], dtype=np.int32), case.scale)
+        if f is not None:
+            out = oracle.fp8.paged_prefill_fp8(*args, f.k_scale[g:g + 1], f.v_scale[g:g + 1], 1, case.dtype)
         else:
+            out = oracle.paged_prefill(*args, 1, case.dtype)
+    else:
+        args = (case.query[b:b + 1, hs], kp, vp, case.block_tables[b:b + 1], case.context_lens[b:b + 1],
+                case.scale)
+        if f is not None:
+            out = oracle.fp8.paged_decode_fp8(*args, f.k_scale[g:g + 1], f.v_scale[g:g + 1], 1, case.dtype)
+        else:
+            out = oracle.paged_decode(*args, 1, case.dtype)
+    return b, g, out
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def cpu_baseline(ctx, budget_s: float, workers: int):
+    """Time the oracle on a bounded sample of the workload: whole passes over the batch (every
+    (sequence, kv head) unit once per pass, in a seeded order) until ``budget_s`` is spent, at
+    least one pass. ``workers`` processes are forked now, before any GPU call in this process;
+    each pass is one ``map`` over the pool, and the pool is closed and joined, never terminated
+    with work in flight. Returns (record, {(b, g): rows}) for the parity check against the GPU
+    output."""
+    import multiprocessing as mp
+    global _UNITS
+    _UNITS = ctx
+    case = ctx["case"]
+    B, H = case.num_seqs, case.num_kv_heads
+    order = [(int(b), g) for b in np.random.default_rng(0).permutation(B) for g in range(H)]
+    units, passes = {}, 0
+    t0 = time.perf_counter()
+    if workers <= 1:
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            for bg in order:
+                b, g, out = _oracle_unit(bg)
+                units[(b, g)] = out
             passes += 1
-            continue
-        break
+    else:
+        pool = mp.get_context("fork").Pool(workers, initializer=_one_blas_thread)
+        try:
+            while passes == 0 or time.perf_counter() - t0 < budget_s:
+                for b, g, out in pool.map(_oracle_unit, order, chunksize=1):
+                    units[(b, g)] = out
+                passes += 1
+        finally:
+            pool.close()
+            pool.join()
     secs = time.perf_counter() - t0
-    unit = "query-tokens/s" if call.startswith("prefill") else "seq-steps/s"
-    return {"value": units / secs, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} sequence-steps ({passes} whole passes over the {case.num_seqs}-sequence batch "
-                      f"plus {len(done) - passes * case.num_seqs} sequences), all heads, fp64 NumPy, {secs:.1f} s",
-            "max_abs_err_vs_gpu": err}
+    _UNITS = None
+    prefill = ctx["prefill"]
+    if prefill:
+        value, unit = passes * int(case.q_lens.sum()) / secs, "query-tokens/s"
+    else:
+        value, unit = passes * B / secs, "seq-steps/s"
+    rec = {"value": value, "unit": unit, "cores": int(workers), "kind": "oracle",
+           "sample": f"{passes} whole pass{'es' if passes > 1 else ''} over the {B}-sequence batch "
+                     f"({'prefill chunks' if prefill else 'decode steps'}) as {passes * len(order)} "
+                     f"(sequence, kv head) units, fp64 NumPy, {workers} process{'es' if workers > 1 else ''} "
+                     f"x 1 BLAS thread, {secs:.1f} s"}
+    return rec, units
+
+
+def oracle_error(case, prefill: bool, units: dict, gpu_out: np.ndarray) -> float:
+    """Largest |gpu - oracle| over the rows the CPU baseline computed."""
+    G = case.num_q_heads // case.num_kv_heads
+    err = 0.0
+    for (b, g), ref in units.items():
+        if prefill:
+            q0, q1 = int(case.cu_q_lens[b]), int(case.cu_q_lens[b + 1])
+            got = gpu_out[q0:q1, g * G:(g + 1) * G]
+        else:
+            got = gpu_out[b:b + 1, g * G:(g + 1) * G]
+        if got.size:
+            err = max(err, float(np.abs(got - ref).max()))
+    return err
 
 
 # ----------------------------------------------------------------------------
@@ -467,18 +530,88 @@ def bench_block_copy(args) -> int:
     return 0
 
 
+# The default run: the long-context split-KV decode is the headline line (the largest
+# single-GPU decode workload, 2.8 GB of KV per step), the other workloads are records in the
+# same run.
+HEADLINE = "long_ctx_bf16_splitkv_b8"
+DEFAULT_SET = [HEADLINE, "tiny_fp32_decode_b4", "llama2_7b_fp16_decode_b64", "llama3_8b_gqa_bf16_decode_b256",
+               "chunked_prefill_bf16_16x2048p512"]
+# workloads that also get a single-core oracle figure
+SINGLE_CORE = {"tiny_fp32_decode_b4", "llama2_7b_fp16_decode_b64", "llama3_8b_gqa_bf16_decode_b256"}
+
+
+def time_workload(args, name: str, case, call: str, host: dict) -> dict:
+    """Upload one workload, time ``args.steps`` steps and return its record."""
+    import torch
+    r = Runner(case, call, args.layers, args.partition, args.step_mode, host.get("fp8"))
+    calibration_copy(args.copy_calibration_mib)
+    elapsed, attn_ms = time_steps(r, args.steps, args.warmup)
+    attn_us = float(np.mean(attn_ms)) * 1e3
+    rec = {"workload": name, "kernel": call, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": elapsed * 1e3 / args.steps, "dtype": case.dtype}
+    cfg = {"workload": name, "kernel": call, "step_mode": args.step_mode, "block_size": 16,
+           "num_seqs": case.num_seqs, "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+           "head_dim": case.head_dim, "kv_pool_replicas": args.layers}
+    if call.startswith("prefill"):
+        flops = prefill_flops(case)
+        rec.update({"value": case.num_q_tokens * args.steps / elapsed, "unit": "query-tokens/s"})
+        achieved = flops / (attn_us * 1e-6) / 1e12
+        rec["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                           "traffic": stored_traffic(name, call, args.partition)}
+        rec["prefill_causal_flops_per_step"] = flops
+        cfg.update({"prior_tokens": int(case.prior_lens[0]), "chunk_tokens": int(case.q_lens[0]), "causal": True})
+    else:
+        ab_unique = decode_bytes(case, True, call)
+        kv_logical, kv_unique = kv_bytes(case, False, call), kv_bytes(case, True, call)
+        rec.update({"value": case.num_seqs * args.steps / elapsed, "unit": "seq-steps/s"})
+        achieved = ab_unique / (attn_us * 1e-6) / 1e9
+        rec["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS,
+                           "traffic": stored_traffic(name, call, args.partition)}
+        rec["kv_gb_per_s"] = {"logical": kv_logical / (attn_us * 1e-6) / 1e9,
+                              "unique": kv_unique / (attn_us * 1e-6) / 1e9}
+        rec["hbm_peak_frac"] = achieved / HBM_PEAK_GBPS
+        rec["algorithmic_bytes_per_launch"] = ab_unique
+        cfg.update({"context_tokens": int(case.context_lens.astype(np.int64).sum()),
+                    "max_context_len": case.max_context_len})
+        if call.startswith("splitkv"):
+            cfg["partition_size"] = args.partition
+        if call.endswith("_fp8"):
+            cfg["kv_cache_dtype"] = "fp8_e4m3"
+    rec["attention_us_per_launch"] = attn_us
+    rec["scatter_bytes_per_step"] = scatter_bytes(case, call)
+    rec["config"] = cfg
+    cb = host.get("cpu_baseline")
+    if cb is not None:
+        gpu_out = r.out.float().cpu().double().numpy()
+        cb = dict(cb)
+        cb["max_abs_err_vs_gpu"] = oracle_error(case, call.startswith("prefill"), host["units"], gpu_out)
+    rec["cpu_baseline"] = cb
+    del r
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS),
+                    help="time only this workload (default: the headline workload plus the other "
+                         "configurations as records of the same line)")
     ap.add_argument("--kernel", default=None,
                     choices=["decode", "splitkv", "prefill", "decode_fp8", "splitkv_fp8", "prefill_fp8"],
-                    help="attention entry point (default: the workload's)")
+                    help="attention entry point (default: the workload's; with --workload only)")
     ap.add_argument("--partition", type=int, default=512, help="split-KV partition size (tokens)")
     ap.add_argument("--layers", type=int, default=4, help="KV pool replicas rotated over steps")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=5.0,
+                    help="seconds of oracle work per workload for cpu_baseline (and again for the "
+                         "single-core figure where one is taken)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (default: the CPUs this process may run on)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-mode", default="separate", choices=["separate", "fused", "graph"],
                     help="separate: scatter launch + attention launch; fused: one pa_decode_step launch; "
@@ -492,72 +625,74 @@ def main(argv=None) -> int:
               "MI355X; run it with --gpus 1.", file=sys.stderr)
         return 2
 
-    import torch
     import workloads as W
 
     if args.workload in BLOCK_WORKLOADS:
         return bench_block_copy(args)
-    gen_key, call = WORKLOADS[args.workload]
-    call = args.kernel or call
-    t_gen = time.perf_counter()
-    case = W.NAMED[gen_key]()
-    t_gen = time.perf_counter() - t_gen
-    if args.step_mode != "separate" and call not in ("decode", "decode_fp8"):
-        print("--step-mode fused/graph applies to the single-pass decode workloads", file=sys.stderr)
+    names = [args.workload] if args.workload else DEFAULT_SET
+    if args.kernel and not args.workload:
+        print("--kernel needs --workload", file=sys.stderr)
+        return 2
+    if args.step_mode != "separate" and not all(WORKLOADS[n][1] in ("decode", "decode_fp8") or args.kernel
+                                                for n in names):
+        print("--step-mode fused/graph applies to the single-pass decode workloads: pass --workload",
+              file=sys.stderr)
         return 2
     if args.step_mode == "graph" and args.steps % args.layers:
         print("--step-mode graph replays all layers at once: --steps must be a multiple of --layers",
               file=sys.stderr)
         return 2
-    r = Runner(case, call, args.layers, args.partition, args.step_mode)
-    print(f"# workload {args.workload}: generated in {t_gen:.1f} s, kernel {call}", file=sys.stderr, flush=True)
-    calibration_copy(args.copy_calibration_mib)
+    workers = args.cpu_workers or len(os.sched_getaffinity(0))
 
-    elapsed, attn_ms = time_steps(r, args.steps, args.warmup)
-    attn_us = float(np.mean(attn_ms)) * 1e3
-    step_ms = elapsed * 1e3 / args.steps
+    # host phase (no GPU call yet): inputs, and the oracle's CPU baseline on them. This
+    # process keeps one BLAS thread, so the workers it forks inherit no BLAS thread pool.
+    _one_blas_thread()
+    hosts = {}
+    for name in names:
+        gen_key, call = WORKLOADS[name]
+        call = args.kernel or call
+        t_gen = time.perf_counter()
+        case = W.NAMED[gen_key]()
+        t_gen = time.perf_counter() - t_gen
+        fp8_host = W.fp8_pools(case, 0) if call.endswith("_fp8") else None
+        host = {"case": case, "call": call, "fp8": fp8_host, "cpu_baseline": None, "units": {}}
+        if not args.no_cpu_baseline:
+            ctx = _unit_ctx(case, call, fp8_host)
+            rec, units = cpu_baseline(ctx, args.cpu_budget, workers)
+            if name in SINGLE_CORE:
+                one, _ = cpu_baseline(ctx, args.cpu_budget, 1)
+                rec["single_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+            del ctx
+            host.update(cpu_baseline=rec, units=units)
+            print(f"# {name}: oracle baseline {rec['value']:.4g} {rec['unit']} ({rec['sample']})",
+                  file=sys.stderr, flush=True)
+        hosts[name] = host
+        print(f"# workload {name}: generated in {t_gen:.1f} s, kernel {call}", file=sys.stderr, flush=True)
 
+    records = {}
+    for name in names:
+        h = hosts.pop(name)
+        records[name] = time_workload(args, name, h["case"], h["call"], h)
+        print(f"# {name}: {records[name]['attention_us_per_launch']:.1f} us per launch, "
+              f"roofline {records[name]['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+
+    head = records[names[0]]
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": case.dtype, "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)"}
-    cfg = {"workload": args.workload, "kernel": call, "step_mode": args.step_mode, "block_size": 16,
-           "num_seqs": case.num_seqs,
-           "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
-           "kv_pool_replicas": args.layers}
-    if call.startswith("prefill"):
-        flops = prefill_flops(case)
-        tokens = case.num_q_tokens
-        res.update({"value": tokens * args.steps / elapsed, "unit": "query-tokens/s"})
-        achieved = flops / (attn_us * 1e-6) / 1e12
-        res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
-                           "traffic": stored_traffic(args.workload, call, args.partition)}
-        res["prefill_causal_flops_per_step"] = flops
-        cfg.update({"prior_tokens": int(case.prior_lens[0]), "chunk_tokens": int(case.q_lens[0]), "causal": True})
-    else:
-        ab_unique = decode_bytes(case, True, call)
-        kv_logical, kv_unique = kv_bytes(case, False, call), kv_bytes(case, True, call)
-        res.update({"value": case.num_seqs * args.steps / elapsed, "unit": "seq-steps/s"})
-        achieved = ab_unique / (attn_us * 1e-6) / 1e9
-        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS,
-                           "traffic": stored_traffic(args.workload, call, args.partition)}
-        res["kv_gb_per_s"] = {"logical": kv_logical / (attn_us * 1e-6) / 1e9,
-                              "unique": kv_unique / (attn_us * 1e-6) / 1e9}
-        res["hbm_peak_frac"] = achieved / HBM_PEAK_GBPS
-        res["algorithmic_bytes_per_launch"] = ab_unique
-        cfg.update({"context_tokens": int(case.context_lens.astype(np.int64).sum()),
-                    "max_context_len": case.max_context_len})
-        if call.startswith("splitkv"):
-            cfg["partition_size"] = args.partition
-        if call.endswith("_fp8"):
-            cfg["kv_cache_dtype"] = "fp8_e4m3"
-            res["data"] = ("synthetic (seeded N(0,1) queries and new K/V, uniform e4m3 cache codes with "
-                           "per-head scales, shuffled physical blocks)")
-    res["attention_us_per_launch"] = attn_us
-    res["scatter_bytes_per_step"] = scatter_bytes(case, call)
-    res["config"] = cfg
-    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(case, call, r, args.cpu_budget)
+           "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": head["dtype"],
+           "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)",
+           "value": head["value"], "unit": head["unit"], "roofline": head["roofline"]}
+    for k in ("kv_gb_per_s", "hbm_peak_frac", "algorithmic_bytes_per_launch", "prefill_causal_flops_per_step",
+              "attention_us_per_launch", "scatter_bytes_per_step"):
+        if k in head:
+            res[k] = head[k]
+    if head["kernel"].endswith("_fp8"):
+        res["data"] = ("synthetic (seeded N(0,1) queries and new K/V, uniform e4m3 cache codes with "
+                       "per-head scales, shuffled physical blocks)")
+    res["config"] = head["config"]
+    res["cpu_baseline"] = head["cpu_baseline"]
+    if len(names) > 1:
+        res["configs"] = {n: records[n] for n in names[1:]}
     print(json.dumps(res), flush=True)
     return 0
 

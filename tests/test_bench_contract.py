@@ -91,3 +91,36 @@ def test_committed_traffic_records_are_consistent(workload):
         sum(v * rec["write_scale"] * 1024 for v in rec["write_kib_per_dispatch"].values())
     assert abs(total - rec["hbm_bytes_per_launch"]) <= 1e-6 * total + 2
     assert 1.9 < rec["fetch_scale"] < 2.1 and 0.95 < rec["write_scale"] < 1.05
+
+
+@pytest.mark.parametrize("maker,call", [(lambda: W.make_decode("cb", "bf16", [5, 40, 300], 8, 2, 64, seed=3),
+                                         "splitkv"),
+                                        (lambda: W.make_prefill("cbp", "bf16", [20, 0], [9, 33], 8, 2, 64, seed=4),
+                                         "prefill")])
+def test_cpu_baseline_units_reassemble_the_oracle(maker, call):
+    """The CPU baseline splits a step into (sequence, kv head) units, each the oracle on one kv
+    head's slice of the pools; in two worker processes the units must cover the batch and
+    reassemble the oracle's whole-batch output exactly, and the record must state the worker
+    count that ran them."""
+    import numpy as np
+    import oracle
+    case = maker()
+    ctx = bench._unit_ctx(case, call)
+    rec, units = bench.cpu_baseline(ctx, 0.5, 2)
+    assert rec["cores"] == 2 and rec["kind"] == "oracle" and rec["value"] > 0
+    assert set(units) == {(b, g) for b in range(case.num_seqs) for g in range(case.num_kv_heads)}
+    if call == "prefill":
+        full = oracle.paged_prefill(case.query, ctx["kp"], ctx["vp"], case.block_tables, case.seq_lens,
+                                    case.cu_q_lens, case.scale, case.num_kv_heads, case.dtype)
+    else:
+        full = oracle.paged_decode(case.query, ctx["kp"], ctx["vp"], case.block_tables, case.context_lens,
+                                   case.scale, case.num_kv_heads, case.dtype)
+    assert bench.oracle_error(case, call == "prefill", units, full) == 0.0
+    one, _ = bench.cpu_baseline(ctx, 0.2, 1)
+    assert one["cores"] == 1
+
+
+def test_default_run_has_the_headline_first():
+    assert bench.DEFAULT_SET[0] == bench.HEADLINE == "long_ctx_bf16_splitkv_b8"
+    assert set(bench.DEFAULT_SET[1:]) == {"tiny_fp32_decode_b4", "llama2_7b_fp16_decode_b64",
+                                          "llama3_8b_gqa_bf16_decode_b256", "chunked_prefill_bf16_16x2048p512"}
