@@ -335,11 +335,24 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
   // and V(t+1) into the other two buffers; one barrier per tile.
   f32x16 sa[2], sb[2];                       // scores of two consecutive tiles
   dma(0, entry(0), 0, 0, entry(0), 0);
+  // Does any block with visible keys lack a valid table entry? Checked once,
+  // with vector loads that complete with the first tile's, so that only a
+  // workgroup that has such a block pays the per-tile lookups of tile_bad.
+  bool any_bad = (kend + kBlockSize - 1) / kBlockSize > p.block_table_stride;
+  {
+    int bad = 0;
+    const int32_t* row = p.block_tables + (int64_t)b * p.block_table_stride;
+    for (int i = lane; i < nblk_valid; i += 64) {
+      const int bid = row[i];
+      bad |= (bid < 0 || bid >= p.num_blocks);
+    }
+    any_bad = any_bad || __any(bad);
+  }
   land(0, 0, v_ok(0, entry(0)));
   dma(1, entry(1), 1, nkt, entry(nkt), 1);    // K(1); the V part re-reads tile nkt-1 into sV[1]
   // table entries for the loads of the next iteration, read a tile ahead
   int kbid_next = entry(2), vbid_next = entry(1);
-  int bad_cur = tile_bad(0);                 // blocks of the scored tile without a valid entry
+  int bad_cur = any_bad ? tile_bad(0) : 0;   // blocks of the scored tile without a valid entry
   {
     const uint8_t* K0 = sK[0];
 #pragma unroll
@@ -364,18 +377,24 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     const bool vok_next = v_ok(t + 1, vbid_next);
 
     // scale; mask (uniform: only tiles that reach the causal diagonal or the
-    // end of the keys, or hold a block without a valid table entry); tile max
-    // of the column; rare rescale
-    const bool edge = (key0 + kBK > kend) || (p.causal && key0 + kBK - 1 > s0 + q0) || bad_cur != 0;
+    // end of the keys); tile max of the column; rare rescale
+    const bool edge = (key0 + kBK > kend) || (p.causal && key0 + kBK - 1 > s0 + q0);
     if (edge) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool vis = key < kend && (!p.causal || key <= pabs) && !((bad_cur >> (2 * kt + (r >> 3))) & 1);
+          const bool vis = key < kend && (!p.causal || key <= pabs);
           sc[kt][r] = vis ? sc[kt][r] : -INFINITY;
         }
+    }
+    if (bad_cur) {                            // uniform and rare: blocks without a valid entry
+#pragma unroll
+      for (int k = 0; k < kBK / kBlockSize; ++k)
+        if ((bad_cur >> k) & 1)               // block k of the tile = registers 8(k&1).. of half k>>1
+#pragma unroll
+          for (int r = 0; r < 8; ++r) sc[k >> 1][8 * (k & 1) + r] = -INFINITY;
     }
     // tile max of the column (raw scores, scale > 0) by a balanced tree of
     // 3-input maxima; rare rescale
@@ -500,7 +519,7 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
     }
     kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
     vbid_next = entry(t + 2);                 // loads complete during the wait below
-    bad_cur = t + 1 < nkt ? tile_bad(t + 1) : 0;
+    bad_cur = (any_bad && t + 1 < nkt) ? tile_bad(t + 1) : 0;
     land(t + 1, (t + 1) & 1, vok_next);
   };
   int t = 0;
