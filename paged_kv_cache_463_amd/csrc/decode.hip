@@ -493,7 +493,7 @@ void decode_kernel(DecodeParams p) {
   static_assert(G <= LPR, "group larger than a row of lanes");
   using HM = HeadMap<G>;
 
-  __shared__ float s_acc[W][G][D];
+  __shared__ __attribute__((aligned(16))) float s_acc[W][G][D];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
   __shared__ int s_plan[GROUP ? kPlanInts : 1];
@@ -818,48 +818,70 @@ void decode_kernel(DecodeParams p) {
       if (i + k * STEP < hi) process(i + k * STEP, kbuf[k], vbuf[k], okb[k]);
   }
 
-  // sum the ROWS row-streams of the wave (lanes of one c share the head order)
+  // Sum the ROWS row-streams of the wave (lanes of one c share the head
+  // order). l is summed in full. The accumulators are reduce-scattered: at the
+  // exchange with lane ^ o (o = 32, 16, .., LPR) a lane keeps one half of the
+  // values it still holds and hands the other half to its partner, so after
+  // log2(ROWS) exchanges it owns NV = G*EPL/ROWS consecutive values (flattened
+  // index head position * EPL + element) starting at vbase, which it stores
+  // with wide writes; all 64 lanes store.
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
-    l += __shfl_xor(l, o);
+  for (int o = LPR; o < 64; o <<= 1) l += __shfl_xor(l, o);
+  constexpr int NV = G * EPL / ROWS;
+  float vals[G * EPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+    for (int e = 0; e < EPL; ++e) vals[h * EPL + e] = acc[h][e];
+  int vbase = 0;
+#pragma unroll
+  for (int o = 32, n = G * EPL; o >= LPR; o >>= 1, n >>= 1) {
+    const bool up = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float send = up ? vals[i] : vals[i + n / 2];
+      const float keep = up ? vals[i + n / 2] : vals[i];
+      vals[i] = keep + __shfl_xor(send, o);
+    }
+    vbase += up ? n / 2 : 0;
   }
   if constexpr (F8) {
     const float vs = p.v_scale[g];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= vs;
+    for (int i = 0; i < NV; ++i) vals[i] *= vs;
   }
+  // the run of CW values at run index i: head position (vbase + i) / EPL,
+  // elements from (vbase + i) % EPL (NV and EPL are multiples of CW)
+  constexpr int CW = NV >= 4 ? 4 : NV;
+  static_assert(NV % CW == 0 && EPL % CW == 0, "runs stay inside one head's row");
+  auto store_run = [&](float* dst, int i) {
+    if constexpr (CW == 4) *reinterpret_cast<f32x4*>(dst) = f32x4{vals[i], vals[i + 1], vals[i + 2], vals[i + 3]};
+    else if constexpr (CW == 2) *reinterpret_cast<float2*>(dst) = float2{vals[i], vals[i + 1]};
+    else *dst = vals[i];
+  };
   if constexpr (MODE == kWaveItems) {       // the wave's partial goes straight to the workspace
-    if (r == 0) {
-      const int64_t row0 = (int64_t)b * p.num_q_heads + hq0;
+    const int64_t row0 = (int64_t)b * p.num_q_heads + hq0;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int64_t pr = (row0 + (h ^ own)) * p.max_parts + part;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) p.ws_acc[pr * D + c * EPL + e] = acc[h][e];
-      }
-      if (c < G) {                          // lanes 0..G-1 own distinct heads
-        const int64_t pr = (row0 + own) * p.max_parts + part;
-        p.ws_ml[2 * pr] = m_ref;
-        p.ws_ml[2 * pr + 1] = l;
-      }
+    for (int i = 0; i < NV; i += CW) {
+      const int v = vbase + i, hp = v / EPL, e = v % EPL;
+      const int64_t pr = (row0 + (hp ^ own)) * p.max_parts + part;
+      store_run(p.ws_acc + pr * D + c * EPL + e, i);
+    }
+    if (r == 0 && c < G) {                  // lanes 0..G-1 own distinct heads
+      const int64_t pr = (row0 + own) * p.max_parts + part;
+      p.ws_ml[2 * pr] = m_ref;
+      p.ws_ml[2 * pr + 1] = l;
     }
     return;
   }
-  if (r == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h ^ own][c * EPL + e] = acc[h][e];
-    if (c < G) {                            // lanes 0..G-1 own distinct heads
-      s_m[wave][own] = m_ref;
-      s_l[wave][own] = l;
-    }
+  for (int i = 0; i < NV; i += CW) {
+    const int v = vbase + i, hp = v / EPL, e = v % EPL;
+    store_run(&s_acc[wave][hp ^ own][c * EPL + e], i);
+  }
+  if (r == 0 && c < G) {                    // lanes 0..G-1 own distinct heads
+    s_m[wave][own] = m_ref;
+    s_l[wave][own] = l;
   }
   __syncthreads();
 
