@@ -540,6 +540,34 @@ DEFAULT_SET = [HEADLINE, "tiny_fp32_decode_b4", "llama2_7b_fp16_decode_b64", "ll
 SINGLE_CORE = {"tiny_fp32_decode_b4", "llama2_7b_fp16_decode_b64", "llama3_8b_gqa_bf16_decode_b256"}
 
 
+def time_read_probe(r: Runner, steps: int, warmup: int) -> dict:
+    """Time pa_read_kv_rows over the same pools, tables and walk as the attention call (its
+    K/V rows with the same loads and no arithmetic): the practical read ceiling of that access
+    set. Bytes counted are those it reads: every table block of every sequence, whole."""
+    import workloads as W
+    torch, P, case = r.torch, r.P, r.case
+    part = r.partition if r.call.startswith("splitkv") else 0
+    waves = 4 * (case.num_kv_heads * case.num_seqs * (W.ceil_div(max(case.max_context_len, 1), part) if part else 1))
+    sink = torch.zeros(max(waves, 1), dtype=torch.int32, device="cuda")
+    mcl = max(case.max_context_len, 1)
+    for i in range(warmup):
+        P.read_kv_rows(r.kp[i % r.layers], r.vp[i % r.layers], r.bt, r.lens, mcl, part, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        P.read_kv_rows(r.kp[i % r.layers], r.vp[i % r.layers], r.bt, r.lens, mcl, part, sink)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    blocks = sum(W.ceil_div(int(L), W.BLOCK_SIZE) for L in case.context_lens)
+    nbytes = blocks * W.BLOCK_SIZE * 2 * case.num_kv_heads * case.head_dim * kv_elem_bytes(case, r.call)
+    return {"us_per_launch": us, "bytes_per_launch": nbytes, "gb_per_s": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "walk": "split-KV" if part else "single pass"}
+
+
 def time_workload(args, name: str, case, call: str, host: dict) -> dict:
     """Upload one workload, time ``args.steps`` steps and return its record."""
     import torch
@@ -579,6 +607,10 @@ def time_workload(args, name: str, case, call: str, host: dict) -> dict:
             cfg["partition_size"] = args.partition
         if call.endswith("_fp8"):
             cfg["kv_cache_dtype"] = "fp8_e4m3"
+        if not args.no_read_probe and args.step_mode == "separate":
+            rp = time_read_probe(r, args.steps, args.warmup)
+            rp["attention_time_over_probe"] = attn_us / rp["us_per_launch"]
+            rec["read_probe"] = rp
     rec["attention_us_per_launch"] = attn_us
     rec["scatter_bytes_per_step"] = scatter_bytes(case, call)
     rec["config"] = cfg
@@ -613,6 +645,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="oracle worker processes (default: the CPUs this process may run on)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip timing the read-only pass over the same K/V rows (decode workloads)")
     ap.add_argument("--step-mode", default="separate", choices=["separate", "fused", "graph"],
                     help="separate: scatter launch + attention launch; fused: one pa_decode_step launch; "
                          "graph: the fused step replayed from a HIP graph (single-pass decode only)")
@@ -683,7 +717,7 @@ def main(argv=None) -> int:
            "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)",
            "value": head["value"], "unit": head["unit"], "roofline": head["roofline"]}
     for k in ("kv_gb_per_s", "hbm_peak_frac", "algorithmic_bytes_per_launch", "prefill_causal_flops_per_step",
-              "attention_us_per_launch", "scatter_bytes_per_step"):
+              "attention_us_per_launch", "scatter_bytes_per_step", "read_probe"):
         if k in head:
             res[k] = head[k]
     if head["kernel"].endswith("_fp8"):

@@ -497,6 +497,29 @@ PA_API int32_t pa_prefill_chunked_fp8(void* out, const void* query, const int32_
                                float scale, int32_t causal, const float* k_scale, const float* v_scale,
                                int32_t dtype, void* stream);
 
+/*
+ * pa_read_kv_rows — read-bandwidth calibration beside the attention calls, not
+ * part of the attention path: reads exactly the K and V rows that pa_decode
+ * (partition_size == 0) or pa_decode_splitkv (partition_size > 0, the same
+ * partitions) would read for these arguments — every cached token's row of
+ * every kv head, through the block tables — with the same 16-byte
+ * non-temporal loads and no arithmetic. Each wave stores an XOR of the words
+ * it read into sink[some index < sink_words] (so the reads cannot be dropped;
+ * the values carry no meaning). Timing it next to an attention call on the
+ * same cache measures how fast the memory system delivers that access set.
+ *
+ *   cache_elem_bytes  1 (FP8 cache), 2 (f16/bf16) or 4 (f32)
+ *   sink              device uint32 [sink_words], sink_words >= 1
+ * Other arguments as pa_decode_splitkv; the split-KV walk supports up to 1024
+ * sequences (PA_ERR_UNSUPPORTED beyond). Out-of-range table entries are read
+ * as block 0; nothing outside the pools and sink is addressed.
+ */
+PA_API int32_t pa_read_kv_rows(const void* k_cache, const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                               const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t cache_elem_bytes,
+                               int32_t max_context_len, int32_t partition_size, uint32_t* sink, int64_t sink_words,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     lib,
     prefill_chunked,
     prefill_chunked_fp8,
+    read_kv_rows,
     reshape_and_cache,
     reshape_and_cache_fp8,
     splitkv_workspace_bytes,
@@ -32,5 +33,5 @@ from ._binding import (  # noqa: F401
 __all__ = ["reshape_and_cache", "decode", "decode_splitkv", "splitkv_workspace_bytes",
            "reshape_and_cache_fp8", "decode_fp8", "decode_splitkv_fp8", "decode_step", "decode_step_fp8",
            "decode_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "StepGraph",
-           "prefill_chunked", "prefill_chunked_fp8", "copy_blocks", "swap_blocks", "BlockManager", "lib", "LIB_PATH",
+           "prefill_chunked", "prefill_chunked_fp8", "copy_blocks", "swap_blocks", "read_kv_rows", "BlockManager", "lib", "LIB_PATH",
            "LibraryNotBuilt", "PagedAttentionError"]

@@ -38,6 +38,7 @@ SIGNATURES = {
                                  _f32, _i32, _i32, _i32, _p, _sz, _p]),
     "pa_decode_splitkv_noalloc": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _i32, _i32, _i32, _p]),
+    "pa_read_kv_rows": (_i32, [_p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _i64, _p]),
     "pa_prefill_chunked": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, _i32, _p]),
     "pa_prefill_chunked_fp8": (_i32, [_p, _p, _p, _i32, _i64, _p, _p, _i64, _i64, _p, _i32, _p, _i32, _i32,
@@ -247,6 +248,25 @@ def decode_splitkv_noalloc(out: torch.Tensor, query: torch.Tensor, k_cache: torc
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, bs, scale, _dtype(query),
         max_context_len, partition_size, _stream(stream)))
+
+
+def read_kv_rows(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, max_context_len: int, partition_size: int,
+                 sink: torch.Tensor, stream=None) -> None:
+    """Read-bandwidth calibration: read the K/V rows a decode (partition_size 0) or split-KV
+    decode would read, with no arithmetic; ``sink`` is a device int32/uint32 tensor."""
+    nb, bs, hkv, d, bstride = _pool_dims(k_cache)
+    _pools_match(k_cache, v_cache)
+    _i32_tensor(block_tables, "block_tables")
+    _i32_tensor(context_lens, "context_lens")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == context_lens.numel(), "table rows")
+    _require(sink.dtype in (torch.int32, torch.uint32) and sink.is_contiguous() and sink.numel() > 0, "sink")
+    _on_device(("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+               ("context_lens", context_lens), ("sink", sink))
+    _check("pa_read_kv_rows", lib().pa_read_kv_rows(
+        _ptr(k_cache), _ptr(v_cache), bstride, nb, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), context_lens.numel(), hkv, d, k_cache.element_size(), max_context_len,
+        partition_size, _ptr(sink), sink.numel(), _stream(stream)))
 
 
 def _new_rows(key: torch.Tensor, value: torch.Tensor, hkv: int, d: int) -> None:

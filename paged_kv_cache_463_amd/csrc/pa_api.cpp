@@ -332,6 +332,41 @@ int32_t pa_decode_splitkv_noalloc(void* out, const void* query, const void* k_ca
   return hip_status(pa::launch_decode_splitkv(p, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_read_kv_rows(const void* k_cache, const void* v_cache, int64_t block_stride, int64_t num_blocks,
+                        const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t cache_elem_bytes,
+                        int32_t max_context_len, int32_t partition_size, uint32_t* sink, int64_t sink_words,
+                        void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_blocks < 0 || block_table_stride < 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (cache_elem_bytes != 1 && cache_elem_bytes != 2 && cache_elem_bytes != 4) return PA_ERR_DTYPE;
+  if (partition_size < 0 || partition_size % 16 != 0) return PA_ERR_SHAPE;
+  if (block_stride < (int64_t)16 * num_kv_heads * head_dim) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PA_ERR_NULL_PTR;
+  if (num_blocks == 0 || block_table_stride == 0 || sink_words <= 0) return PA_ERR_SHAPE;
+  if (partition_size > 0 && num_seqs > 1024) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (block_stride * cache_elem_bytes) % 16 != 0)
+    return PA_ERR_ALIGNMENT;
+  pa::ReadProbeParams p{};
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_stride_bytes = block_stride * cache_elem_bytes;
+  p.num_blocks = num_blocks;
+  p.block_tables = block_tables;
+  p.block_table_stride = block_table_stride;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.row_bytes = head_dim * cache_elem_bytes;
+  p.partition_blocks = partition_size / 16;
+  p.max_parts = partition_size > 0 ? (int32_t)ceil_div(max_context_len > 0 ? max_context_len : 1, partition_size) : 0;
+  p.sink = sink;
+  p.sink_words = sink_words;
+  return hip_status(pa::launch_read_probe(p, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pa_decode_step(void* out, const void* query, const void* key_new, const void* value_new,
                        int64_t kv_token_stride, void* k_cache, void* v_cache, int64_t block_stride,
                        int64_t num_blocks, const int32_t* block_tables, int32_t block_table_stride,

@@ -104,6 +104,25 @@ struct SwapChunk {
   int32_t pairs[kSwapChunk][2]; // (source, destination), checked on the host
 };
 
+// read-bandwidth calibration (read_probe.hip)
+struct ReadProbeParams {
+  const void* k_cache;
+  const void* v_cache;
+  int64_t block_stride_bytes;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t block_table_stride;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t row_bytes;            // head_dim * cache element bytes (128, 256 or 512)
+  int32_t partition_blocks;     // split-KV walk: partition_size / 16; 0: single-pass walk
+  int32_t max_parts;            // ceil(max_context_len / partition_size) (split-KV walk)
+  uint32_t* sink;
+  int64_t sink_words;
+};
+hipError_t launch_read_probe(const ReadProbeParams& p, hipStream_t s);
+
 hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t s);
 hipError_t launch_swap_chunk(const SwapChunk& c, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
