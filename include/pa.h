@@ -243,7 +243,7 @@ PA_API int32_t pa_decode_step(void* out, const void* query, const void* key_new,
  * tables, K/V, queries) is read at replay, so one graph serves every step of
  * a batch size whose buffers keep their addresses. A captured split-KV call
  * also freezes its max_context_len and the plan derived from it (partition
- * count, workspace layout, workgroup or wave items): capture it with a
+ * count, workspace layout, workgroup, span or wave items): capture it with a
  * max_context_len that bounds the lengths of every later replay, since a
  * sequence that grows past it is cut at the planned partitions (see
  * pa_decode_splitkv). Recordable calls: those

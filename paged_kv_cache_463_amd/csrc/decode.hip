@@ -38,15 +38,21 @@
 //   * Block ids are wave-uniform (scalar loads, read a step ahead); two register
 //     buffers keep the next block's K/V loads in flight while a block is computed.
 //
-// Split-KV: a (kv head, sequence, partition p) item covers logical tokens
-// [partition_size*p, partition_size*(p+1)) and writes, per query head, the
-// unnormalised output row plus (max, normaliser) to the workspace; a second
-// kernel merges partitions by log-sum-exp. Two plans, chosen by the number of
-// partitions a sequence can have: above 16, every wave walks one item on its
-// own (wave items, see split_work); up to 16, a workgroup walks one item with
-// its waves taking the blocks round-robin and a one-partition sequence is
-// written directly (workgroup items, see group_work). Items are handed out by
-// a work counter in both.
+// Split-KV: partition p of a sequence covers logical tokens
+// [partition_size*p, partition_size*(p+1)); its unnormalised output row and
+// (max, normaliser) per query head are merged by log-sum-exp. Three plans,
+// chosen by the number of partitions a sequence can have and the cache type:
+//   * up to 16 (short and mixed contexts): workgroup items. A workgroup walks
+//     one (kv head, sequence, partition) item with its waves taking the
+//     blocks round-robin; a one-partition sequence is written directly.
+//   * more, 16-bit caches: span items. A workgroup takes W consecutive
+//     partitions of one (kv head, sequence), wave w walks the w-th on its
+//     own, and the W partials are merged in LDS before one row per head goes
+//     to the workspace (a sequence with a single span is written directly).
+//   * more, fp8 cache: wave items. Every wave walks one partition on its own
+//     and writes its partial straight to the workspace (see split_work).
+// A second kernel merges what reached the workspace. Items are handed out by
+// a work counter in all three.
 #include <math.h>
 
 #include <algorithm>
@@ -54,15 +60,6 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
-#ifndef PA_SPLITKV_WAVES
-#define PA_SPLITKV_WAVES 4
-#endif
-#ifndef PA_DECODE_ROTATE
-#define PA_DECODE_ROTATE 1
-#endif
 
 namespace pa {
 
@@ -282,12 +279,18 @@ __device__ __forceinline__ int sequence_of_row(const int32_t* lens, int B, int r
   return __builtin_amdgcn_readfirstlane(s_pick);
 }
 
-// Partitions of a sequence of L tokens, at most max_parts: a sequence longer
-// than the max_context_len the call was planned for (a precondition
-// violation) is cut there rather than written past the workspace.
-__device__ __forceinline__ int parts_of(const DecodeParams& p, int L) {
+// Blocks a split-KV call walks for a sequence of L tokens, at most the
+// max_parts planned partitions: a sequence longer than the max_context_len the
+// call was planned for (a precondition violation) is cut there rather than
+// written past the workspace.
+__device__ __forceinline__ int split_blocks(const DecodeParams& p, int L) {
   const int nb = min((max(L, 0) + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-  return min((nb + p.partition_blocks - 1) / p.partition_blocks, p.max_parts);
+  return min(nb, p.max_blocks);
+}
+
+// Work units (partitions, or spans of partitions) of a sequence of L tokens.
+__device__ __forceinline__ int parts_of(const DecodeParams& p, int L) {
+  return (split_blocks(p, L) + p.partition_blocks - 1) / p.partition_blocks;
 }
 
 // 64 lanes turn v[0..n) into its exclusive prefix sums in place, v[n] = total.
@@ -380,7 +383,7 @@ __global__ void splitkv_reset_kernel(int32_t* ctr) {
 // exclusive prefix sums pre[] of the partition counts in rank order. Batches
 // above kRankMaxSeqs sequences number all num_seqs * max_parts pairs in
 // sequence order instead (empty pairs are skipped).
-enum : int { kSingle = 0, kWaveItems = 1, kGroupItems = 2 };
+enum : int { kSingle = 0, kWaveItems = 1, kGroupItems = 2, kSpanItems = 3 };
 constexpr int kPlanCur = kBuckets;                       // [0, kBuckets): bucket bases
 constexpr int kPlanPre = 2 * kBuckets;                   // bucket members, then pre[0..B]
 constexpr int kPlanPerm = kPlanPre + kRankMaxSeqs + 1;   // perm[rank] = sequence
@@ -477,7 +480,8 @@ template <DT dt, DT kt, int D, int G, int W, int MODE, int NB>
 __global__ __launch_bounds__(64 * W)
 void decode_kernel(DecodeParams p) {
   constexpr bool SPLIT = MODE != kSingle;
-  constexpr bool GROUP = MODE == kGroupItems;
+  constexpr bool GROUP = MODE == kGroupItems || MODE == kSpanItems;   // workgroup items, LDS merge
+  constexpr bool SPAN = MODE == kSpanItems;
   constexpr bool F8 = kt == DT::FP8;        // e4m3 cache, widened to dt on the fly
   static_assert(F8 || kt == dt, "a 16-bit or fp32 cache has the query's type");
   static_assert(!F8 || dt != DT::F32, "an fp8 cache is read with 16-bit queries");
@@ -557,10 +561,11 @@ void decode_kernel(DecodeParams p) {
   }
 
   const int L = max(MODE == kSingle ? Lb : p.context_lens[b], 0);
-  const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
+  const int nblk = SPLIT ? split_blocks(p, L) : min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
   // single pass and workgroup items: the W waves share the blocks round-robin.
   // wave items: every wave walks one partition on its own (no merge across waves)
-  constexpr int STEP = MODE == kWaveItems ? 1 : W;
+  // span items: every wave walks one partition of the span on its own
+  constexpr int STEP = MODE == kWaveItems || SPAN ? 1 : W;
   int lo = 0, hi = nblk;
   if constexpr (SPLIT) {
     lo = part * p.partition_blocks;
@@ -573,6 +578,11 @@ void decode_kernel(DecodeParams p) {
       }
     }
     hi = min(nblk, lo + p.partition_blocks);
+    if constexpr (SPAN) {                   // wave w: the w-th partition of the span (may be empty)
+      const int sub = p.partition_blocks / W;
+      lo = min(lo + wave * sub, hi);
+      hi = min(hi, lo + sub);
+    }
   }
 
   // this lane's 16-byte slice of the G query vectors, position i = head i ^ own
@@ -613,17 +623,16 @@ void decode_kernel(DecodeParams p) {
   // unconditionally (a conditional load would make the compiler's wait counts
   // drain the prefetch of every block), and re-reading the block a wave has
   // just read is an L2 hit.
-  // Walk order: with PA_DECODE_ROTATE the waves of a workgroup start at a
-  // per-sequence offset into the blocks and wrap around, so sequences that
-  // share physical blocks do not all read them at the same moment. Scores
-  // and masks follow the logical block, so only the summation order changes.
+  // Walk order: where the waves of a workgroup share a range round-robin
+  // (single pass, workgroup items) they start at a per-sequence offset into
+  // it and wrap around, so sequences that share physical blocks do not all
+  // read them at the same moment. Scores and masks follow the logical block,
+  // so only the summation order changes.
   int rot = 0;
-#if PA_DECODE_ROTATE
-  if constexpr (MODE != kWaveItems) {
+  if constexpr (MODE == kSingle || MODE == kGroupItems) {
     const int span = hi - lo;
     rot = span > 1 ? (int)(((uint32_t)b * 2654435761u) >> 8) % span : 0;
   }
-#endif
   auto logical = [&](int i) -> int { return i + rot >= hi ? i + rot - (hi - lo) : i + rot; };
   auto block_id = [&](int i) -> int { return tbl[logical(min(i, hi - 1))]; };
   // K/V rows are read once per call: non-temporal loads keep them from
@@ -784,7 +793,7 @@ void decode_kernel(DecodeParams p) {
   // to be used.
   KR kbuf[NB][TPL], vbuf[NB][TPL];
   bool okb[NB];
-  const int first = MODE == kWaveItems ? lo : lo + wave;
+  const int first = MODE == kWaveItems || SPAN ? lo : lo + wave;
   if (first < hi) {
     // buffers issued in order (an empty asm that clobbers memory keeps the
     // loads of buffer k+1 behind those of buffer k), as inside the loop
@@ -932,9 +941,7 @@ void splitkv_merge_kernel(DecodeParams p) {
   __shared__ float s_den[NPG];
   const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int col = (t % TPR) * 4, grp = t / TPR;
-  const int L = max(p.context_lens[b], 0);
-  const int nblk = min((L + kBlockSize - 1) / kBlockSize, p.block_table_stride);
-  const int np = min((nblk + p.partition_blocks - 1) / p.partition_blocks, p.max_parts);
+  const int np = parts_of(p, p.context_lens[b]);
   if (DIRECT1 && np == 1) return;                  // written by the partition pass itself
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
   const float* ml = p.ws_ml + row * p.max_parts * 2;
@@ -974,36 +981,20 @@ void splitkv_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-// Register buffers of K/V blocks in flight per wave (bytes in flight per CU
-// bound the bandwidth: the large-group kernels run fewer waves per SIMD).
-#ifndef PA_DECODE_NB_SMALLG
-#define PA_DECODE_NB_SMALLG 2
-#endif
-#ifndef PA_DECODE_NB_LARGEG
-#define PA_DECODE_NB_LARGEG 2
-#endif
-#ifndef PA_DECODE_NB_FP8
-#define PA_DECODE_NB_FP8 4
-#endif
-constexpr int decode_buffers(DT dt, DT kt, int D, int G) {
-  // an fp8 buffer holds half the bytes of a 16-bit one
-  return kt == DT::FP8 ? PA_DECODE_NB_FP8
-                       : (dt == DT::F32 && D == 128) ? 2 : (G >= 4 ? PA_DECODE_NB_LARGEG : PA_DECODE_NB_SMALLG);
-}
+// Register buffers of K/V blocks in flight per wave: two of a 16-bit or fp32
+// cache, four of an fp8 cache (whose buffer holds half the bytes).
+constexpr int decode_buffers(DT kt) { return kt == DT::FP8 ? 4 : 2; }
 
-// Waves per workgroup; fp32 with head_dim 128 holds twice the bytes per lane
-// and stays at 4 waves so that its registers fit without spilling.
-template <DT dt, int D, int MODE>
-constexpr int decode_waves() {
-  return (dt == DT::F32 && D == 128) ? 4 : (MODE == kWaveItems ? PA_SPLITKV_WAVES : PA_DECODE_WAVES);
-}
+// Waves per workgroup.
+constexpr int kDecodeWaves = 4;
 
 // Split-KV takes workgroup items when no sequence has more than this many
-// partitions (short or mixed contexts); beyond it nearly every item is a whole
-// partition and one wave per item needs no merge across waves.
-#ifndef PA_GROUP_MAX_PARTS
-#define PA_GROUP_MAX_PARTS 16
-#endif
+// partitions (short or mixed contexts). Beyond it nearly every item is a whole
+// partition: a 16-bit cache takes span items (W partitions per workgroup,
+// merged in LDS, so a quarter of the partial rows reach the workspace), an
+// fp8 cache wave items (its waves spend longer per block, and the barrier
+// of the LDS merge costs more than the stores it saves).
+constexpr int kGroupMaxParts = 16;
 
 // Persistent grid of the workgroup-item kernel: as many workgroups as the chip
 // holds at once, never more than there can be items.
@@ -1018,16 +1009,21 @@ static int64_t resident_grid(K kernel, int threads, int64_t items) {
 }
 
 template <DT dt, DT kt, int D, int G, int MODE>
-static hipError_t launch_mode(const DecodeParams& p, hipStream_t s) {
-  constexpr int W = decode_waves<dt, D, MODE>();
-  auto kernel = decode_kernel<dt, kt, D, G, W, MODE, decode_buffers(dt, kt, D, G)>;
+static hipError_t launch_mode(const DecodeParams& p_in, hipStream_t s) {
+  constexpr int W = kDecodeWaves;
+  auto kernel = decode_kernel<dt, kt, D, G, W, MODE, decode_buffers(kt)>;
+  // span items: the kernel and the merge see spans of W partitions as their
+  // unit (the workspace keeps its stride of max_parts partition slots)
+  DecodeParams p = p_in;
+  p.max_blocks = p_in.max_parts * p_in.partition_blocks;
+  if constexpr (MODE == kSpanItems) p.partition_blocks = W * p_in.partition_blocks;
   dim3 grid(p.num_kv_heads, p.num_seqs, 1);
   if constexpr (MODE != kSingle) {          // work items are handed out by a counter
     const int64_t items = (int64_t)p.num_kv_heads * p.num_seqs * p.max_parts;
     if (items + items / 4 + 64 * W > 0x7FFFFFFF) return hipErrorInvalidValue;   // tickets fit int32
     hipLaunchKernelGGL(splitkv_reset_kernel, dim3(1), dim3(64), 0, s, p.ws_ctr);
     int64_t wgs;
-    if constexpr (MODE == kGroupItems) {
+    if constexpr (MODE == kGroupItems || MODE == kSpanItems) {
       wgs = resident_grid(kernel, 64 * W, items);
       if (wgs < 0) return hipErrorInvalidValue;
     } else {
@@ -1038,7 +1034,7 @@ static hipError_t launch_mode(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || MODE == kSingle) return e;
-  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D, MODE == kGroupItems>), dim3(p.num_q_heads, p.num_seqs),
+  hipLaunchKernelGGL((splitkv_merge_kernel<dt, D, MODE != kWaveItems>), dim3(p.num_q_heads, p.num_seqs),
                      dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -1082,7 +1078,8 @@ static hipError_t launch_any(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) { return launch_any<kSingle>(p, s); }
 hipError_t launch_decode_splitkv(const DecodeParams& p, hipStream_t s) {
-  return p.max_parts <= PA_GROUP_MAX_PARTS ? launch_any<kGroupItems>(p, s) : launch_any<kWaveItems>(p, s);
+  if (p.max_parts <= kGroupMaxParts) return launch_any<kGroupItems>(p, s);
+  return p.kv_dtype == kKvFp8 ? launch_any<kWaveItems>(p, s) : launch_any<kSpanItems>(p, s);
 }
 
 }  // namespace pa

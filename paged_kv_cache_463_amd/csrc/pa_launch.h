@@ -56,6 +56,7 @@ struct DecodeParams {
   // split-KV only
   int32_t partition_blocks;     // partition_size / 16
   int32_t max_parts;            // ceil(max_context_len / partition_size)
+  int32_t max_blocks;           // blocks walked per sequence at most (set by the launcher)
   float* ws_acc;                // [num_seqs][num_q_heads][max_parts][head_dim]
   float* ws_ml;                 // [num_seqs][num_q_heads][max_parts][2]  (max, normaliser)
   int32_t* ws_ctr;              // work counter of the partition kernel (zeroed per call)

@@ -1,11 +1,14 @@
 """GPU parity of pa_decode_splitkv (partition pass + log-sum-exp merge) through the C ABI.
 
-The library plans in one of two ways from max_context_len / partition_size: up to 16 partitions
+The library plans from max_context_len / partition_size and the cache type: up to 16 partitions
 per sequence, a workgroup walks one (kv head, sequence, partition) item and a sequence with a
-single partition is written directly; above that, one wave walks one partition and every
-sequence goes through the merge. Tests name the mode they reach; passing a max_context_len
-above the longest sequence (a valid bound) raises the planned partition count and forces the
-wave mode on the same inputs."""
+single partition is written directly (workgroup items); above that, a workgroup takes four
+consecutive partitions, one per wave, merges them in LDS and sends one partial per span to the
+merge, a single-span sequence being written directly (span items). An fp8 cache above 16
+partitions takes wave items instead (one wave per partition, every partial to the merge; its
+tests are with the fp8 ones). Tests name the mode they reach; passing a max_context_len above
+the longest sequence (a valid bound) raises the planned partition count and forces span items
+on the same inputs."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype,G,D", [("bf16", 8, 128), ("f16", 1, 128), ("f32", 4, 64), ("bf16", 2, 64)])
-@pytest.mark.parametrize("part", [16, 64, 512])     # 94 and 24 partitions: wave items; 3: workgroup items
+@pytest.mark.parametrize("part", [16, 64, 512])     # 94 and 24 partitions: span items; 3: workgroup items
 def test_splitkv_shapes(dtype, G, D, part):
     hkv = 2 if G < 8 else 1
     case = W.make_decode("split", dtype, [1, 16, 17, 100, 511, 512, 513, 1500], G * hkv, hkv, D,
@@ -33,12 +36,12 @@ def test_splitkv_shapes(dtype, G, D, part):
     assert_close(out_f64(out), oracle_decode(case, kp, vp), dtype, f"splitkv part={part}")
 
 
-@pytest.mark.parametrize("mode,span,part", [("group", 97, 32), ("wave", 297, 16)])
+@pytest.mark.parametrize("mode,span,part", [("group", 97, 32), ("span", 297, 16)])
 def test_splitkv_batch_above_dense_numbering_limit(mode, span, part):
     """Above 1024 sequences the work items number every (sequence, partition) pair, empty ones
     included; every output row must still be written once and right (the output starts NaN).
     Lengths up to 97 in 32-token partitions plan 4 partitions (workgroup items); up to 297 in
-    16-token partitions, 19 (wave items)."""
+    16-token partitions, 19 (span items)."""
     lens = [(13 * i) % span + 1 for i in range(1100)]
     case = W.make_decode("splitbig", "bf16", lens, 4, 2, 64, seed=41)
     say(f"case: splitkv {mode} items B={case.num_seqs} part={part}")
@@ -54,8 +57,9 @@ def test_single_partition_agrees_with_single_pass():
     """A partition covering the whole sequence is the same softmax as the single pass. With
     workgroup items it is also the same decomposition (four waves taking the blocks
     round-robin, the same merge of the waves, the output written directly), so the bits agree.
-    With wave items (forced by a larger max_context_len) one wave sums the partition and the
-    merge normalises it, so that result agrees to rounding (and with the oracle), not bit for bit."""
+    With span items (forced by a larger max_context_len) one wave sums the whole partition and
+    the merge of the span normalises it, so that result agrees to rounding (and with the oracle),
+    not bit for bit."""
     case = W.make_decode("onepart", "bf16", [3, 90, 400, 1000], 32, 8, 128, seed=31)
     d = DeviceDecode(case)
     d.scatter()
@@ -67,14 +71,14 @@ def test_single_partition_agrees_with_single_pass():
     ref = oracle_decode(case, kp, vp)
     assert_close(out_f64(a), ref, "bf16", "single pass")
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "workgroup item != single pass"
-    assert_close(out_f64(c), ref, "bf16", "one partition, wave item")
+    assert_close(out_f64(c), ref, "bf16", "one partition, span item")
     assert_close(out_f64(a), out_f64(c), "bf16", "single pass vs one partition")
 
 
 @pytest.mark.parametrize("dtype,G,D", [("bf16", 4, 128), ("f16", 1, 128), ("f32", 8, 64)])
 def test_splitkv_item_modes_agree_with_oracle(dtype, G, D):
     """The same inputs through both plans: workgroup items (max_context_len = the longest
-    sequence, 4 partitions of 512) and wave items (max_context_len raised to 20 partitions).
+    sequence, 4 partitions of 512) and span items (max_context_len raised to 20 partitions).
     Lengths straddle partition edges, include 0 and 1, and sequences with one partition (written
     directly) sit beside ones that go through the merge."""
     lens = [0, 1, 15, 16, 17, 511, 512, 513, 1024, 1025, 2000, 1536, 300, 47]
@@ -89,7 +93,7 @@ def test_splitkv_item_modes_agree_with_oracle(dtype, G, D):
     kp, vp = assert_scatter_exact(case, d.kp, d.vp)
     ref = oracle_decode(case, kp, vp)
     assert_close(out_f64(grp), ref, dtype, "workgroup items")
-    assert_close(out_f64(wav), ref, dtype, "wave items")
+    assert_close(out_f64(wav), ref, dtype, "span items")
     assert not out_f64(grp)[0].any() and not out_f64(wav)[0].any()
     short = [i for i, L in enumerate(lens) if 0 < L <= 512]
     bits = torch.int32 if dtype == "f32" else torch.int16
@@ -163,7 +167,7 @@ def test_workspace_too_small_is_rejected():
 
 def test_long_context_bf16_full_size():
     """The long-context batch at full size (8 sequences of 32k-131k tokens, 64 query / 8 kv heads,
-    512-token partitions, wave items): every sequence and head against the oracle."""
+    512-token partitions, span items): every sequence and head against the oracle."""
     case = W.long_context_bf16()
     say(f"case: long context split-KV, all sequences, lens {case.context_lens.tolist()}")
     d = DeviceDecode(case)
@@ -175,7 +179,7 @@ def test_long_context_bf16_full_size():
     assert_close(out_f64(out), oracle_decode(case, kp, vp), "bf16", "long-context split-KV, all sequences")
 
 
-@pytest.mark.parametrize("part", [512, 32])        # 2 partitions planned: workgroup items; 32: wave items
+@pytest.mark.parametrize("part", [512, 32])        # 2 partitions planned: workgroup items; 32: span items
 def test_sequence_longer_than_planned_stays_inside_the_workspace(part):
     """max_context_len is a bound the caller promises; a sequence beyond it (a precondition
     violation) is cut at the planned partitions instead of being written past the workspace.

@@ -110,12 +110,12 @@ def test_step_graph_replays_a_growing_batch():
     graph.close()
 
 
-@pytest.mark.parametrize("plan", ["group", "wave"])
+@pytest.mark.parametrize("plan", ["group", "span"])
 def test_step_graph_of_splitkv_and_fp8_step(plan):
     """A graph holding a split-KV decode (its counter reset is a kernel, not a memset) and
     an FP8 fused step, replayed three times with eager work between; every replay equals
     the eager calls bit for bit. max_context_len = the longest sequence plans 6 partitions of
-    512 (workgroup items); 20 partitions' worth plans wave items."""
+    512 (workgroup items); 20 partitions' worth plans span items."""
     case = W.make_decode("gsplit", "bf16", [100, 1500, 3000, 17], 16, 2, 128, seed=160)
     d = DeviceDecode(case)
     d.scatter()
@@ -144,7 +144,7 @@ def test_step_graph_of_splitkv_and_fp8_step(plan):
     graph.close()
 
 
-@pytest.mark.parametrize("plan", ["group", "wave"])
+@pytest.mark.parametrize("plan", ["group", "span"])
 def test_splitkv_graph_replays_while_lengths_grow(plan):
     """A split-KV call captured once with max_context_len set to the largest length the batch
     will reach (the plan, grid and workspace layout are frozen at capture) serves later replays

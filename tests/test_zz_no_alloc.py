@@ -48,7 +48,7 @@ def _pair(case, part, mcl):
 
 @pytest.mark.gpu
 def test_noalloc_equals_workspace_call_on_consecutive_calls():
-    """First a long-context batch planned as wave items (many partitions per sequence), then a
+    """First a long-context batch planned as span items (many partitions per sequence), then a
     smaller batch planned as workgroup items; both through the same static scratch."""
     big = W.make_decode("noalloc1", "bf16", [20000, 513, 9000, 16, 31000, 1], 32, 4, 128, seed=71)
     _pair(big, 512, big.max_context_len)
