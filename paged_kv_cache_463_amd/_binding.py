@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PA_LIBRARY names another build of the same library (the host-sanitizer one)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_PTR", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",

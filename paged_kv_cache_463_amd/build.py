@@ -3,6 +3,19 @@
 Every translation unit under ``csrc/`` is compiled to an object in ``_build/``
 (in parallel) and linked into ``paged_kv_cache_463_amd/libpagedattn.so``. The
 library exports only the C ABI declared in ``include/pa.h``.
+
+Host-side sanitizer build (CPU checks only; device code is never built with a
+sanitizer): ``PA_SANITIZE=address python -m paged_kv_cache_463_amd.build``
+compiles the host half of every file under AddressSanitizer into
+``_build/sanitize-address/libpagedattn.so`` and leaves the product library
+alone. Run the host tests against it with the runtime preloaded::
+
+    LD_PRELOAD=$(/opt/rocm/bin/hipcc -print-file-name=libclang_rt.asan-x86_64.so) \
+    ASAN_OPTIONS=detect_leaks=0 PA_LIBRARY=_build/sanitize-address/libpagedattn.so \
+    python -m pytest -m "not gpu" tests/test_abi.py tests/test_block_manager.py tests/test_binding_checks.py
+
+(leak checks are off because the Python interpreter itself is not built with
+the sanitizer and keeps its allocations to the end).
 """
 from __future__ import annotations
 
@@ -34,9 +47,30 @@ def _hipcc() -> str:
 
 
 # Per-file extra flags. The prefill kernel runs with the IEEE mode bit off and
-# no NaN operands assumed: masked scores are -inf selects and every key a tile
-# reads is a cached row, so max() needs no quieting of its inputs.
+# with no NaN operands assumed. Its pools may hold NaN in slots no sequence
+# owns (stale or poisoned rows past a length, whole blocks whose table entry is
+# out of range), so the kernel keeps one invariant: every score of a key that is
+# not visible (causal mask, past the length, or in a block with a bad entry) is
+# replaced by a select of -inf before it reaches a max or an exp, and the V
+# rows of such keys are zero (dead rows of the last block, bad blocks) before
+# they reach a product. No NaN then enters an instruction whose result the
+# flags would let the compiler reorder or drop; a change that lets one through
+# must drop these flags.
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+# Host-side sanitizer (see the module docstring): "address" or "undefined".
+SANITIZE = os.environ.get("PA_SANITIZE", "")
+if SANITIZE:
+    if SANITIZE not in ("address", "undefined"):
+        raise RuntimeError(f"PA_SANITIZE={SANITIZE!r}: expected 'address' or 'undefined'")
+    BUILD = os.path.join(BUILD, "sanitize-" + SANITIZE)
+    LIB = os.path.join(BUILD, "libpagedattn.so")
+    # each sanitizer flag goes to the host compilation only
+    HIP_FLAGS = HIP_FLAGS + ["-Xarch_host", "-fsanitize=" + SANITIZE, "-Xarch_host", "-fno-omit-frame-pointer",
+                             "-Xarch_host", "-g"]
+    LINK_FLAGS = ["-fsanitize=" + SANITIZE, "-shared-libsan"]
+else:
+    LINK_FLAGS = []
 
 
 def _compile(src: str) -> str:
@@ -54,7 +88,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *LINK_FLAGS, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
