@@ -981,9 +981,12 @@ void splitkv_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-// Register buffers of K/V blocks in flight per wave: two of a 16-bit or fp32
-// cache, four of an fp8 cache (whose buffer holds half the bytes).
-constexpr int decode_buffers(DT kt) { return kt == DT::FP8 ? 4 : 2; }
+// Register buffers of K/V blocks in flight per wave. Two for every cache type:
+// an fp8 buffer holds half the bytes, but four of them cost the GQA kernels a
+// wave per SIMD (196 against 164 VGPRs at eight heads a group), which the GQA
+// batch over an fp8 cache paid with 5% (102 against 97 us); three buffers for
+// a 16-bit cache were 4-6% slower on the same batch for the same reason.
+constexpr int kDecodeBuffers = 2;
 
 // Waves per workgroup.
 constexpr int kDecodeWaves = 4;
@@ -1011,7 +1014,7 @@ static int64_t resident_grid(K kernel, int threads, int64_t items) {
 template <DT dt, DT kt, int D, int G, int MODE>
 static hipError_t launch_mode(const DecodeParams& p_in, hipStream_t s) {
   constexpr int W = kDecodeWaves;
-  auto kernel = decode_kernel<dt, kt, D, G, W, MODE, decode_buffers(kt)>;
+  auto kernel = decode_kernel<dt, kt, D, G, W, MODE, kDecodeBuffers>;
   // span items: the kernel and the merge see spans of W partitions as their
   // unit (the workspace keeps its stride of max_parts partition slots)
   DecodeParams p = p_in;
