@@ -982,10 +982,11 @@ void splitkv_merge_kernel(DecodeParams p) {
 // dispatch
 // ---------------------------------------------------------------------------
 // Register buffers of K/V blocks in flight per wave. Two for every cache type:
-// an fp8 buffer holds half the bytes, but four of them cost the GQA kernels a
-// wave per SIMD (196 against 164 VGPRs at eight heads a group), which the GQA
-// batch over an fp8 cache paid with 5% (102 against 97 us); three buffers for
-// a 16-bit cache were 4-6% slower on the same batch for the same reason.
+// an fp8 buffer holds half the bytes, but four of them cost the grouped-query
+// kernels a wave per SIMD (four heads a group: 144 against 118 VGPRs; eight:
+// 196 against 164), which the GQA batch over an fp8 cache paid with 5% (102
+// against 97 us); three buffers for a 16-bit cache were 4-6% slower on the
+// same batch for the same reason.
 constexpr int kDecodeBuffers = 2;
 
 // Waves per workgroup.

@@ -101,9 +101,12 @@ __device__ __forceinline__ V as_vec(const u32x4& u) { return __builtin_bit_cast(
 // F8: K and V come from an FP8 (e4m3) cache. Each wave then loads its block of
 // the tile into registers with ordinary 16-byte loads (issued where the 16-bit
 // path issues its direct global->LDS loads), widens the codes to the query
-// type (exact) when the tile lands, and writes them into LDS in the same
-// swizzled 16-bit layout, so everything after the landing is shared with the
-// 16-bit path. k_scale[g] joins the score scale and v_scale[g] the output.
+// type (exact) and writes them into LDS in the same swizzled 16-bit layout,
+// so everything after the landing is shared with the 16-bit path. Inside the
+// loop the widening runs under the second half of the tile's P.V products
+// (the destination buffers are free by then, and the loads have had the
+// score phase to land), not before the barrier. k_scale[g] joins the score
+// scale and v_scale[g] the output.
 template <DT dt, int D, int G, bool F8>
 __global__ __launch_bounds__(64 * kWaves, 2)
 void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const float* k_scale,
@@ -291,18 +294,21 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
   // wait for this wave's loads; in the last V tile zero the rows of keys past
   // kend (stale slots) in this wave's block, and all rows of a block without a
   // valid table entry, then make everything visible
-  auto land = [&](int tv, int vb, bool vok) {
+  // FP8: widen-and-write unit u (0 .. 4*NL8-1) of this wave's landed rows:
+  // load u/4, K or V, first or second 16-bit granule pair
+  auto widen_unit = [&](int u) {
+    const int i = u >> 2, kv = (u >> 1) & 1, h = u & 1;
+    const int g0 = (q8 * (D / 4) + 16 * i) / 8 + h;
+    const u32x4 w = kv ? v8[i] : k8[i];
+    uint8_t* dst = const_cast<uint8_t*>(kv ? pend_vd : pend_kd) + r8 * RB;
+    const int sw = kv ? vswz(r8) : kswz(r8);
+    *reinterpret_cast<u32x4*>(dst + ((g0 ^ sw) << 4)) = widen_fp8<dt>(u32x2{w[2 * h], w[2 * h + 1]});
+  };
+  auto land = [&](int tv, int vb, bool vok, bool widened = false) {
     if constexpr (F8) {                      // widen this wave's rows into the 16-bit layout
+      if (!widened) {
 #pragma unroll
-      for (int i = 0; i < NL8; ++i) {
-        const int g0 = (q8 * (D / 4) + 16 * i) / 8;
-        const u32x4 kw = k8[i], vw = v8[i];
-        uint8_t* kd = const_cast<uint8_t*>(pend_kd) + r8 * RB;
-        uint8_t* vd = const_cast<uint8_t*>(pend_vd) + r8 * RB;
-        *reinterpret_cast<u32x4*>(kd + ((g0 ^ kswz(r8)) << 4)) = widen_fp8<dt>(u32x2{kw[0], kw[1]});
-        *reinterpret_cast<u32x4*>(kd + (((g0 + 1) ^ kswz(r8)) << 4)) = widen_fp8<dt>(u32x2{kw[2], kw[3]});
-        *reinterpret_cast<u32x4*>(vd + ((g0 ^ vswz(r8)) << 4)) = widen_fp8<dt>(u32x2{vw[0], vw[1]});
-        *reinterpret_cast<u32x4*>(vd + (((g0 + 1) ^ vswz(r8)) << 4)) = widen_fp8<dt>(u32x2{vw[2], vw[3]});
+        for (int u = 0; u < 4 * NL8; ++u) widen_unit(u);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -514,13 +520,22 @@ void prefill_kernel(PrefillParams p, int tiles_per_pair, int xcd_mapped, const f
         }
         const vec pbk = as_vec<vec>(pk[ks >> 1][ks & 1]);
         o[md] = M::run(va[i % 3], pbk, o[md]);
+        // FP8: the next tiles' rows (loaded during the scores above) are
+        // widened into LDS under the second half of the products
+        if constexpr (F8) {
+          constexpr int U = 4 * NL8, H = NV / 2;
+          if (i >= H) {
+#pragma unroll
+            for (int u = (i - H) * U / H; u < (i - H + 1) * U / H; ++u) widen_unit(u);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     kbid_next = entry(t + 3);                 // after this tile's LDS reads: the scalar
     vbid_next = entry(t + 2);                 // loads complete during the wait below
     bad_cur = (any_bad && t + 1 < nkt) ? tile_bad(t + 1) : 0;
-    land(t + 1, (t + 1) & 1, vok_next);
+    land(t + 1, (t + 1) & 1, vok_next, true);
   };
   int t = 0;
   for (; t + 1 < nkt; t += 2) {
