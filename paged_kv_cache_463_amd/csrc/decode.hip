@@ -619,10 +619,10 @@ void decode_kernel(DecodeParams p) {
 
   // block id of logical block i (scalar load); ids are read two steps ahead of
   // their K/V loads so the dependent table lookup never stalls a block. Past
-  // the end the last block is named again: the prefetch below is issued
-  // unconditionally (a conditional load would make the compiler's wait counts
-  // drain the prefetch of every block), and re-reading the block a wave has
-  // just read is an L2 hit.
+  // the end the last block is named again (the lookups and the loads of the
+  // main loop are unconditional: a conditional load there would make the
+  // compiler's wait counts drain the prefetch of every block); re-reading the
+  // block a wave has just read is an L2 hit.
   // Walk order: where the waves of a workgroup share a range round-robin
   // (single pass, workgroup items) they start at a per-sequence offset into
   // it and wrap around, so sequences that share physical blocks do not all
@@ -786,11 +786,16 @@ void decode_kernel(DecodeParams p) {
   // blocks first, first + STEP, ... through NB register buffers: all NB are in
   // flight before the first block is computed, and each buffer is refilled
   // with the block NB steps ahead as soon as it has been consumed. The loop
-  // runs whole rounds of NB blocks and is left only at the end of a round
-  // (the fewer than NB blocks left over are computed after it), so every path
-  // back to the loop head has issued the refills in the same order as the
-  // prologue and the compiler's load counters wait only for the buffer about
-  // to be used.
+  // runs whole rounds of NB blocks and is left only at the end of a round, so
+  // every path back to the loop head has issued the refills in the same order
+  // as the prologue and the compiler's load counters wait only for the buffer
+  // about to be used. Except with workgroup items, whose short round-robin
+  // walks cannot spare the registers, the loop stops one round early so that
+  // its refills all name blocks of the walk, and that last round refills only
+  // the blocks that exist (its conditional loads come after the loop, where a
+  // conservative wait costs nothing) instead of re-reading the last block.
+  // The fewer than NB blocks left are computed last.
+  constexpr bool EXACT_TAIL = MODE != kGroupItems;
   KR kbuf[NB][TPL], vbuf[NB][TPL];
   bool okb[NB];
   const int first = MODE == kWaveItems || SPAN ? lo : lo + wave;
@@ -804,7 +809,7 @@ void decode_kernel(DecodeParams p) {
     }
     int bid = block_id(first + NB * STEP);
     int i = first;
-    for (; i + (NB - 1) * STEP < hi; i += NB * STEP) {
+    for (; i + ((EXACT_TAIL ? 2 : 1) * NB - 1) * STEP < hi; i += NB * STEP) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         process(i + k * STEP, kbuf[k], vbuf[k], okb[k]);
@@ -821,6 +826,23 @@ void decode_kernel(DecodeParams p) {
         okb[k] = fetch(bid, kbuf[k], vbuf[k]);
         bid = block_id(i + (k + NB + 1) * STEP);
       }
+    }
+    if constexpr (EXACT_TAIL) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (i + k * STEP < hi) {
+          process(i + k * STEP, kbuf[k], vbuf[k], okb[k]);
+          if (i + (k + NB) * STEP < hi) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) asm volatile("" : "+v"(acc[h][e])::"memory");
+            okb[k] = fetch(bid, kbuf[k], vbuf[k]);
+            bid = block_id(i + (k + NB + 1) * STEP);
+          }
+        }
+      }
+      i += NB * STEP;
     }
 #pragma unroll
     for (int k = 0; k + 1 < NB; ++k)
