@@ -9,7 +9,10 @@
 //     sequence, partition) item, items numbered kv head fastest and then the
 //     existing (sequence, partition) pairs densely, four waves per workgroup;
 //   * partition_size == 0 (the single-pass walk): one workgroup of four waves
-//     per (kv head, sequence), the waves taking its blocks round-robin.
+//     per (kv head, sequence), the waves taking its blocks round-robin; grid
+//     row r takes the sequence of rank r in descending length (ties by
+//     index), the dispatch order of the single-pass decode, found here by a
+//     direct count (batches above 1024 sequences keep grid order).
 // Each wave keeps two blocks of loads in flight and folds the words it read
 // into an XOR that it stores into sink, so no load can be dropped.
 #include <algorithm>
@@ -22,7 +25,25 @@ namespace pa {
 namespace {
 
 constexpr int kProbeWaves = 4;
-constexpr int kProbeMaxSeqs = 1024;        // dense item numbering in LDS up to this batch
+constexpr int kProbeMaxSeqs = 1024;        // dense item numbering / ranking in LDS up to this batch
+
+// The sequence of rank r (descending length, ties by index) among B <= 1024:
+// keys in LDS, then every thread counts, for its candidates, the keys larger
+// than theirs; the candidate with count r is the one.
+__device__ int probe_sequence_of_rank(const int32_t* lens, int B, int r, int* s_key) {
+  __shared__ int s_pick;
+  for (int t = threadIdx.x; t < B; t += 64 * kProbeWaves)
+    s_key[t] = (min(max(lens[t], 0), (1 << 21) - 1) << 10) | (1023 - t);
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += 64 * kProbeWaves) {
+    const int key = s_key[t];
+    int rank = 0;
+    for (int u = 0; u < B; ++u) rank += s_key[u] > key;
+    if (rank == r) s_pick = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_pick);
+}
 
 template <int TPL>
 __global__ __launch_bounds__(64 * kProbeWaves)
@@ -79,7 +100,7 @@ void read_probe_kernel(ReadProbeParams p) {
     step = 1;
   } else {                                   // single-pass walk: one workgroup per (kv head, sequence)
     g = blockIdx.x;
-    b = blockIdx.y;
+    b = B <= kProbeMaxSeqs ? probe_sequence_of_rank(p.context_lens, B, blockIdx.y, s_pre) : blockIdx.y;
     const int nb = min((max(p.context_lens[b], 0) + kBlockSize - 1) / kBlockSize, p.block_table_stride);
     lo = wave;
     hi = nb;
