@@ -154,9 +154,13 @@ PA_API size_t pa_decode_splitkv_workspace_bytes(int32_t num_seqs, int32_t num_q_
  * The plan follows P = ceil(max_context_len / partition_size). With P <= 16
  * a workgroup computes one (kv head, sequence, partition) at a time and a
  * sequence with a single partition is written directly, bit-identical to
- * pa_decode; with P > 16 one wave computes one partition and every sequence
- * goes through the merge. Either way a call's result depends only on its
- * arguments' values (reruns are bit-identical).
+ * pa_decode. With P > 16 one wave computes one partition; over a 16-bit
+ * cache the four consecutive partitions that one workgroup takes are merged
+ * (by the same log-sum-exp) before they reach the workspace, and a sequence
+ * of at most four partitions is written directly; over an FP8 cache
+ * (pa_decode_splitkv_fp8) every partition goes through the merge. Either
+ * way a call's result depends only on its arguments' values (reruns are
+ * bit-identical).
  *
  * Arguments as pa_decode, plus
  *   max_context_len  upper bound of context_lens (host-known); sequences
