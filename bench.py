@@ -612,6 +612,8 @@ def time_workload(args, name: str, case, call: str, host: dict) -> dict:
             rp["attention_time_over_probe"] = attn_us / rp["us_per_launch"]
             rec["read_probe"] = rp
     rec["attention_us_per_launch"] = attn_us
+    rec["attention_us_stats"] = {"median": float(np.median(attn_ms)) * 1e3, "min": float(np.min(attn_ms)) * 1e3,
+                                 "max": float(np.max(attn_ms)) * 1e3}
     rec["scatter_bytes_per_step"] = scatter_bytes(case, call)
     rec["config"] = cfg
     cb = host.get("cpu_baseline")
@@ -717,7 +719,7 @@ def main(argv=None) -> int:
            "data": "synthetic (seeded N(0,1) K/V/Q, shuffled physical blocks)",
            "value": head["value"], "unit": head["unit"], "roofline": head["roofline"]}
     for k in ("kv_gb_per_s", "hbm_peak_frac", "algorithmic_bytes_per_launch", "prefill_causal_flops_per_step",
-              "attention_us_per_launch", "scatter_bytes_per_step", "read_probe"):
+              "attention_us_per_launch", "attention_us_stats", "scatter_bytes_per_step", "read_probe"):
         if k in head:
             res[k] = head[k]
     if head["kernel"].endswith("_fp8"):
